@@ -1,0 +1,309 @@
+// Stable scatter of token rows into the expert-major buffer padded per
+// expert, optionally quantised to OCP fp8 E4M3 with one fp32 scale per
+// 1x128 block, for gfx950.
+//
+// Tokens are copied into contiguous per-expert buffers that feed the
+// experts, and the row every (token, slot) copy went to is recorded for the
+// combine ("Efficient and Portable Mixture-of-Experts Communication",
+// sections Dispatch and Combine); fp8 tokens travel with their block scaling
+// factors (same page, Dispatch).  That design hands out receive rows with an
+// atomically incremented counter, so its order varies run to run; here the
+// row of slot (t, j) is fixed by the scan: row = first row of (tile(t), e)
+// + rank of t among the tile's tokens that chose e, i.e. ascending token
+// order inside every expert segment.
+//
+// Design for CDNA4: one wavefront per token.  Lanes 0..k-1 resolve the k
+// destination rows, which are then broadcast to scalar registers; the token
+// row is read from HBM once in 16-byte vectors (coalesced across the wave)
+// and written k times.  The fp8 path gives each 128-element block to an
+// aligned group of 16 lanes (8 elements per lane): the block's absolute max
+// is a 16-lane reduction, the scale an IEEE fp32 division, and each lane
+// writes 8 code bytes per destination.  Extra workgroups mark padding rows
+// (row_src = -1) in the same launch.
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+constexpr int kDispatchFillBlocks = 64;
+
+// Resolve the k destination rows of token t; lanes >= k hold -1.  A row
+// outside [0, capacity) -- possible only if counts/offsets/workspace come
+// from different calls -- is dropped rather than written.
+__device__ __forceinline__ int token_row(
+    int t, int lane, int k, int E, long long capacity,
+    const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ slot_rank) {
+  int r = -1;
+  if (lane < k) {
+    const size_t s = (size_t)t * k + lane;
+    const int e = topk_idx[s];
+    if (e >= 0 && e < E) {
+      const int rank = slot_rank[s];
+      r = tile_base[(size_t)(t / kTileT) * E + e] + rank;
+      if (rank < 0 || r < 0 || (long long)r >= capacity) r = -1;
+    }
+  }
+  return r;
+}
+
+// MODE 0: exact copy (x and payload of the same 2- or 4-byte type)
+// MODE 1: bf16 x -> fp8;  MODE 2: fp32 x -> fp8
+template <int KMAX, int MODE>
+__global__ __launch_bounds__(256) void dispatch_kernel(
+    const unsigned char* __restrict__ x, int esize, int T, int H,
+    const int32_t* __restrict__ topk_idx, int k, int E,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ slot_rank, unsigned char* __restrict__ rows,
+    long long capacity, float* __restrict__ row_scales,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ tok_row,
+    int tok_blocks) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if ((int)blockIdx.x >= tok_blocks) {
+    // padding rows of every expert, then every row past offsets[E]
+    const int fb = blockIdx.x - tok_blocks;
+    for (int e = fb; e < E; e += kDispatchFillBlocks) {
+      const long long hi = min((long long)offsets[e + 1], capacity);
+      for (long long r = (long long)offsets[e] + counts[e] + threadIdx.x;
+           r < hi; r += 256)
+        if (r >= 0) row_src[r] = -1;
+    }
+    for (long long r = max((long long)offsets[E], 0LL) + fb * 256 +
+                       threadIdx.x;
+         r < capacity; r += kDispatchFillBlocks * 256)
+      row_src[r] = -1;
+    return;
+  }
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+
+  const int r =
+      token_row(t, lane, k, E, capacity, topk_idx, tile_base, slot_rank);
+  if (lane < k) {
+    tok_row[(size_t)t * k + lane] = r;
+    if (r >= 0) row_src[r] = t;
+  }
+  int rj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    rj[j] = (j < k) ? __builtin_amdgcn_readlane(r, j) : -1;
+
+  if constexpr (MODE == 0) {
+    const size_t rowb = (size_t)H * esize;
+    const int nc = (int)(rowb / 16);
+    const unsigned char* src = x + (size_t)t * rowb;
+    constexpr int U = 2;
+    for (int c0 = 0; c0 < nc; c0 += 64 * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < nc) v[u] = ld16_stream(src + (size_t)c * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (rj[j] < 0) continue;
+        unsigned char* dst = rows + (size_t)rj[j] * rowb;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < nc) st16(dst + (size_t)c * 16, v[u]);
+        }
+      }
+    }
+  } else {
+    const int nc8 = H / 8;                  // 8-element groups per row
+    const int nblk = H / kFp8Block;
+    const unsigned char* src = x + (size_t)t * H * esize;
+    for (int c0 = 0; c0 < nc8; c0 += 64) {
+      const int c = c0 + lane;
+      const bool ok = c < nc8;
+      float f[8];
+      if constexpr (MODE == 1) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 v = ok ? ld16_stream(src + (size_t)c * 16) : z;
+        unpack8_bf16(v, f);
+      } else {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 v0 = ok ? ld16_stream(src + (size_t)c * 32) : z;
+        const u32x4 v1 = ok ? ld16_stream(src + (size_t)c * 32 + 16) : z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = __uint_as_float(v0[i]);
+          f[4 + i] = __uint_as_float(v1[i]);
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = max16_f32(amax);
+      const float s = amax > 0.0f ? amax / kFp8Max : 1.0f;
+      u32x2 q;
+      q.x = e4m3_encode(f[0] / s) | (e4m3_encode(f[1] / s) << 8) |
+            (e4m3_encode(f[2] / s) << 16) | (e4m3_encode(f[3] / s) << 24);
+      q.y = e4m3_encode(f[4] / s) | (e4m3_encode(f[5] / s) << 8) |
+            (e4m3_encode(f[6] / s) << 16) | (e4m3_encode(f[7] / s) << 24);
+      if (ok) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (rj[j] < 0) continue;
+          *reinterpret_cast<u32x2*>(rows + (size_t)rj[j] * H + (size_t)c * 8) = q;
+          if ((lane & 15) == 0)
+            row_scales[(size_t)rj[j] * nblk + c / 16] = s;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fixture
+
+// Stand-in expert for tests and benchmarks: y[r] = sigma[e] * deq(rows[r]).
+// PT: payload 0 f32, 1 bf16, 2 fp8.  YT: output 0 f32, 1 bf16.
+template <int PT, int YT>
+__global__ __launch_bounds__(256) void fixture_kernel(
+    const unsigned char* __restrict__ rows, const float* __restrict__ scales,
+    int H, const int32_t* __restrict__ row_src,
+    const int32_t* __restrict__ offsets, int E,
+    const float* __restrict__ sigma, long long capacity,
+    unsigned char* __restrict__ y) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long r = (long long)blockIdx.x * 4 + wv;
+  if (r >= capacity) return;
+  const int src = row_src[r];
+  const int nc8 = H / 8;
+  const size_t ybytes = YT == 0 ? 4 : 2;
+  unsigned char* yrow = y + (size_t)r * H * ybytes;
+  if (src < 0) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int c = lane; c < nc8; c += 64) {
+      st16(yrow + (size_t)c * 8 * ybytes, z);
+      if (YT == 0) st16(yrow + (size_t)c * 32 + 16, z);
+    }
+    return;
+  }
+  // expert whose segment holds r: the last e with offsets[e] <= r
+  int lo = 0, hi = E;                       // invariant offsets[lo] <= r
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= r) lo = mid; else hi = mid;
+  }
+  const float sg = sigma[lo];
+  for (int c = lane; c < nc8; c += 64) {
+    float f[8];
+    if constexpr (PT == 0) {
+      const unsigned char* p = rows + (size_t)r * H * 4 + (size_t)c * 32;
+      const u32x4 v0 = ld16(p), v1 = ld16(p + 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = __uint_as_float(v0[i]);
+        f[4 + i] = __uint_as_float(v1[i]);
+      }
+    } else if constexpr (PT == 1) {
+      unpack8_bf16(ld16(rows + (size_t)r * H * 2 + (size_t)c * 16), f);
+    } else {
+      const u32x2 q =
+          *reinterpret_cast<const u32x2*>(rows + (size_t)r * H + (size_t)c * 8);
+      const float s = scales[(size_t)r * (H / kFp8Block) + c / 16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = e4m3_decode((q.x >> (8 * i)) & 0xffu) * s;
+        f[4 + i] = e4m3_decode((q.y >> (8 * i)) & 0xffu) * s;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = sg * f[i];
+    if constexpr (YT == 0) {
+      u32x4 v0, v1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v0[i] = __float_as_uint(f[i]);
+        v1[i] = __float_as_uint(f[4 + i]);
+      }
+      st16(yrow + (size_t)c * 32, v0);
+      st16(yrow + (size_t)c * 32 + 16, v1);
+    } else {
+      st16(yrow + (size_t)c * 16, pack8_bf16(f));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int KMAX>
+static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
+                              const unsigned char* x, int esize, int T, int H,
+                              const int32_t* idx, int k, int E,
+                              const int32_t* counts, const int32_t* offsets,
+                              const int32_t* tb, const int32_t* sr,
+                              unsigned char* rows, long long cap, float* sc,
+                              int32_t* row_src, int32_t* tok_row, int tblocks) {
+  if (mode == 0)
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 0>), grid, dim3(256), 0, s, x,
+                       esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
+                       cap, sc, row_src, tok_row, tblocks);
+  else if (mode == 1)
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 1>), grid, dim3(256), 0, s, x,
+                       esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
+                       cap, sc, row_src, tok_row, tblocks);
+  else
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 2>), grid, dim3(256), 0, s, x,
+                       esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
+                       cap, sc, row_src, tok_row, tblocks);
+}
+
+hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
+                           const int32_t* topk_idx, int k, int E,
+                           const int32_t* counts, const int32_t* offsets,
+                           const void* workspace, int pdt, void* rows,
+                           size_t capacity, float* row_scales,
+                           int32_t* row_src, int32_t* tok_row, hipStream_t s) {
+  const int32_t* tb = (const int32_t*)workspace;
+  const int32_t* sr =
+      (const int32_t*)((const unsigned char*)workspace + ws_tile_bytes(T, E));
+  const int esize = xdt == DT_F32 ? 4 : 2;
+  const int mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
+  const int tblocks = (T + 3) / 4;
+  const dim3 grid(tblocks + kDispatchFillBlocks);
+  const unsigned char* xb = (const unsigned char*)x;
+  unsigned char* rb = (unsigned char*)rows;
+  const long long cap = (long long)capacity;
+#define MOE_DISPATCH_K(KV)                                                   \
+  launch_dispatch_k<KV>(mode, grid, s, xb, esize, T, H, topk_idx, k, E,      \
+                        counts, offsets, tb, sr, rb, cap, row_scales,        \
+                        row_src, tok_row, tblocks)
+  if (k <= 1) MOE_DISPATCH_K(1);
+  else if (k <= 2) MOE_DISPATCH_K(2);
+  else if (k <= 4) MOE_DISPATCH_K(4);
+  else if (k <= 8) MOE_DISPATCH_K(8);
+  else MOE_DISPATCH_K(16);
+#undef MOE_DISPATCH_K
+  return hipGetLastError();
+}
+
+hipError_t launch_fixture(const void* rows, int pdt, const float* row_scales,
+                          int H, const int32_t* row_src,
+                          const int32_t* offsets, int E, const float* sigma,
+                          size_t capacity, void* y, int ydt, hipStream_t s) {
+  const dim3 grid((unsigned)((capacity + 3) / 4));
+  const unsigned char* rb = (const unsigned char*)rows;
+  unsigned char* yb = (unsigned char*)y;
+  const long long cap = (long long)capacity;
+#define MOE_FIX(PV, YV)                                                       \
+  hipLaunchKernelGGL((fixture_kernel<PV, YV>), grid, dim3(256), 0, s, rb,     \
+                     row_scales, H, row_src, offsets, E, sigma, cap, yb)
+  const int pt = pdt == DT_F32 ? 0 : (pdt == DT_BF16 ? 1 : 2);
+  const int yt = ydt == DT_F32 ? 0 : 1;
+  if (pt == 0 && yt == 0) MOE_FIX(0, 0);
+  else if (pt == 0) MOE_FIX(0, 1);
+  else if (pt == 1 && yt == 0) MOE_FIX(1, 0);
+  else if (pt == 1) MOE_FIX(1, 1);
+  else if (yt == 0) MOE_FIX(2, 0);
+  else MOE_FIX(2, 1);
+#undef MOE_FIX
+  return hipGetLastError();
+}
+
+}  // namespace moe

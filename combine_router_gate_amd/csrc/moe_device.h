@@ -1,0 +1,131 @@
+// Device helpers for the gfx950 (CDNA4) MoE kernels: 16-byte vector types,
+// bf16 / OCP-E4M3 conversions, order-preserving keys and 16-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kTileT = 64;         // tokens per histogram tile (one bit each)
+constexpr int kFp8Block = 128;     // hidden elements per fp8 scale
+constexpr float kFp8Max = 448.0f;  // largest finite E4M3FN magnitude
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));   // 8 bytes
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+// Streaming load: data read once, kept out of the caches' retained set.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) {
+  return __uint_as_float(packed << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {
+  return __uint_as_float(packed & 0xffff0000u);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 bf16 (one 16-byte vector) <-> 8 fp32
+__device__ __forceinline__ void unpack8_bf16(const u32x4& v, float f[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ u32x4 pack8_bf16(const float f[8]) {
+  u32x4 v;
+  v.x = pack_bf16x2(f[0], f[1]);
+  v.y = pack_bf16x2(f[2], f[3]);
+  v.z = pack_bf16x2(f[4], f[5]);
+  v.w = pack_bf16x2(f[6], f[7]);
+  return v;
+}
+
+// ------------------------------------------------------------------ E4M3
+// OCP 8-bit floating point, E4M3 ("FN") variant: bias 7, 3 mantissa bits,
+// exponent field 0 subnormal (m * 2^-9), S.1111.111 NaN, no infinities.
+
+// Round-to-nearest-even, saturating encode of one fp32 value.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7fffffffu;
+  if (ua > 0x7f800000u) return sign | 0x7fu;          // NaN
+  const float a = __uint_as_float(ua);
+  uint32_t code;
+  if (a >= kFp8Max) {
+    code = 0x7eu;                                     // saturate at 448
+  } else if (a < 0.015625f) {                         // below 2^-6: subnormal
+    // the grid is 2^-9: code = rint(a * 2^9); 8 is the smallest normal
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // keep 3 mantissa bits with round-half-even on the fp32 pattern, then
+    // move the exponent bias from 127 to 7 ((127 - 7) << 3 = 960)
+    const uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
+    code = r - 960u;
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t ef = (c >> 3) & 0xfu, mf = c & 7u;
+  float mag;
+  if (ef == 0) {
+    mag = (float)mf * 0.001953125f;                   // m * 2^-9
+  } else {
+    mag = __uint_as_float(((ef + 120u) << 23) | (mf << 20));
+  }
+  if (ef == 15 && mf == 7) mag = __builtin_nanf("");
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ------------------------------------------------------------------ keys
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ------------------------------------------------------------------ reductions
+
+// Maximum over each aligned group of 16 lanes (all lanes get the result).
+__device__ __forceinline__ unsigned long long max16_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
+    const unsigned long long o = __shfl_xor(v, m, 16);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float max16_f32(float v) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+  return v;
+}
+
+}  // namespace moe

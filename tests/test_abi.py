@@ -1,0 +1,174 @@
+"""C-ABI library: loads, exports every declared symbol, and rejects invalid
+arguments on the host before anything is enqueued.  CPU only.
+
+Pointer arguments here are fake addresses that are never dereferenced: each
+call violates exactly one precondition, so validation returns before any
+kernel launch.  The tests skip on a machine with a GPU, where a validation
+bug would launch a kernel on those addresses; GPU-side error handling is
+covered with real tensors in the GPU tests.
+"""
+import ctypes
+
+import pytest
+
+from combine_router_gate_amd import moe
+from combine_router_gate_amd import build as B
+from oracle import moe_oracle as O
+
+OK, NULL, SHAPE, DTYPE, ALIGN, CAP, WS, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+@pytest.fixture(scope="module")
+def L():
+    import os
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("library not built")
+    return moe.lib()
+
+
+@pytest.fixture(scope="module")
+def no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run only without a GPU")
+
+
+def test_exports_every_header_symbol(L):
+    names = moe.header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    dl = ctypes.CDLL(B.LIB_PATH)
+    for n in ["moe_route", "moe_plan", "moe_dispatch", "moe_combine_residual"]:
+        assert getattr(dl, n) is not None
+
+
+def test_status_strings(L):
+    for s in [OK, NULL, SHAPE, DTYPE, ALIGN, CAP, WS, ALIAS, -8]:
+        txt = moe.moe_status_string(s)
+        assert txt and "unknown" not in txt
+    assert "unknown" in moe.moe_status_string(-99)
+
+
+@pytest.mark.parametrize("T,E,k,pad", [(64, 8, 2, 1), (4096, 8, 2, 128),
+                                       (128, 256, 8, 128), (16384, 256, 8, 128),
+                                       (8192, 384, 8, 128), (0, 8, 2, 4)])
+def test_capacity_formula(L, T, E, k, pad):
+    assert moe.moe_rows_capacity(T, E, k, pad) == O.rows_capacity(T, E, k, pad)
+
+
+def test_capacity_invalid(L):
+    assert moe.moe_rows_capacity(10, 4, 5, 1) == 0      # k > E
+    assert moe.moe_rows_capacity(10, 0, 1, 1) == 0
+    assert moe.moe_rows_capacity(10, 513, 2, 1) == 0
+    assert moe.moe_rows_capacity(10, 8, 17, 1) == 0
+    assert moe.moe_rows_capacity(10, 8, 2, 0) == 0
+    assert moe.moe_rows_capacity(2 ** 30, 8, 8, 1) == 0  # rows overflow int32
+
+
+def test_workspace_bytes(L):
+    assert moe.moe_workspace_bytes(0, 8, 2) == 0
+    w = moe.moe_workspace_bytes(16384, 256, 8)
+    assert w >= 4 * (256 * 256 + 16384 * 8)
+    assert moe.moe_workspace_bytes(65, 8, 2) >= 4 * (2 * 8 + 65 * 2)
+
+
+# fake, 256-aligned, far-apart device addresses (never dereferenced)
+A = [0x10000000 * (i + 1) for i in range(16)]
+
+
+def _route(L, **kw):
+    a = dict(x=A[0], xdt=1, T=100, H=256, w=A[1], E=16, bias=None, k=2, pad=4,
+             idx=A[2], tw=A[3], counts=A[4], offsets=A[5], dbg=None, ws=A[6],
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    return L.moe_route(a["x"], a["xdt"], a["T"], a["H"], a["w"], a["E"],
+                       a["bias"], a["k"], a["pad"], a["idx"], a["tw"],
+                       a["counts"], a["offsets"], a["dbg"], a["ws"], a["wsb"],
+                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(idx=None), NULL),
+    (dict(counts=None), NULL), (dict(ws=None), NULL),
+    (dict(k=17), SHAPE), (dict(k=0), SHAPE), (dict(E=0), SHAPE),
+    (dict(E=513), SHAPE), (dict(k=20, E=16), SHAPE), (dict(H=12), SHAPE),
+    (dict(H=0), SHAPE), (dict(T=-1), SHAPE), (dict(pad=0), SHAPE),
+    (dict(xdt=2), DTYPE), (dict(xdt=7), DTYPE),
+    (dict(x=A[0] + 8), ALIGN), (dict(w=A[1] + 4), ALIGN),
+    (dict(wsb=100), WS),
+    (dict(tw=A[0]), ALIAS), (dict(idx=A[1] + 64), ALIAS),
+    (dict(dbg=A[4]), ALIAS), (dict(ws=A[5]), ALIAS),
+])
+def test_route_validation(L, no_gpu, kw, want):
+    assert _route(L, **kw) == want
+
+
+def _dispatch(L, **kw):
+    a = dict(x=A[0], xdt=1, T=100, H=256, idx=A[1], k=2, E=16, pad=4,
+             counts=A[2], offsets=A[3], ws=A[4], wsb=1 << 20, pdt=1,
+             rows=A[5], cap=O.rows_capacity(100, 16, 2, 4), scales=None,
+             row_src=A[6], tok_row=A[7], stream=None)
+    a.update(kw)
+    return L.moe_dispatch(a["x"], a["xdt"], a["T"], a["H"], a["idx"], a["k"],
+                          a["E"], a["pad"], a["counts"], a["offsets"], a["ws"],
+                          a["wsb"], a["pdt"], a["rows"], a["cap"], a["scales"],
+                          a["row_src"], a["tok_row"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(rows=None), NULL), (dict(row_src=None), NULL),
+    (dict(pdt=2), NULL),                       # fp8 without scales
+    (dict(scales=A[8]), DTYPE),                # scales without fp8
+    (dict(pdt=0), DTYPE), (dict(xdt=2, pdt=2, scales=A[8]), DTYPE),
+    (dict(pdt=2, scales=A[8], H=200), SHAPE),  # fp8 needs H % 128 == 0
+    (dict(cap=O.rows_capacity(100, 16, 2, 4) - 1), CAP),
+    (dict(wsb=10), WS), (dict(rows=A[5] + 4), ALIGN),
+    (dict(rows=A[0]), ALIAS), (dict(tok_row=A[1]), ALIAS),
+    (dict(row_src=A[4] + 128), ALIAS), (dict(k=0), SHAPE),
+])
+def test_dispatch_validation(L, no_gpu, kw, want):
+    assert _dispatch(L, **kw) == want
+
+
+def _combine(L, **kw):
+    a = dict(y=A[0], ydt=1, H=256, y_rows=1000, tok_row=A[1], tw=A[2], T=100,
+             k=2, shared=A[3], res_in=A[4], res_out=A[5], rnr=A[6], out=None,
+             odt=1, stream=None)
+    a.update(kw)
+    return L.moe_combine_residual(a["y"], a["ydt"], a["H"], a["y_rows"],
+                                  a["tok_row"], a["tw"], a["T"], a["k"],
+                                  a["shared"], a["res_in"], a["res_out"],
+                                  a["rnr"], a["out"], a["odt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(y=None), NULL), (dict(rnr=None), NULL), (dict(res_out=None), NULL),
+    (dict(out=A[7]), ALIAS),                                  # out with residual
+    (dict(res_in=None, res_out=None, rnr=None), NULL),        # no out at all
+    (dict(res_in=None, out=A[7]), ALIAS),                     # stray residual_out
+    (dict(res_in=None, res_out=None, rnr=None, out=A[7], odt=2), DTYPE),
+    (dict(ydt=2), DTYPE), (dict(H=100), SHAPE), (dict(k=17), SHAPE),
+    (dict(y=A[0] + 4), ALIGN), (dict(res_out=A[5] + 2), ALIGN),
+    (dict(rnr=A[4]), ALIAS), (dict(res_out=A[4] + 256), ALIAS),
+    (dict(res_out=A[3]), ALIAS), (dict(rnr=A[0]), ALIAS),
+])
+def test_combine_validation(L, no_gpu, kw, want):
+    assert _combine(L, **kw) == want
+
+
+def test_plan_validation(L, no_gpu):
+    cap_ok = dict(idx=A[0], T=10, k=2, E=8, pad=1, counts=A[1], offsets=A[2],
+                  ws=A[3], wsb=1 << 16)
+
+    def call(**kw):
+        a = dict(cap_ok)
+        a.update(kw)
+        return L.moe_plan(a["idx"], a["T"], a["k"], a["E"], a["pad"],
+                          a["counts"], a["offsets"], a["ws"], a["wsb"], None)
+    assert call(idx=None) == NULL
+    assert call(counts=None) == NULL
+    assert call(k=9) == SHAPE
+    assert call(wsb=1) == WS
+    assert call(counts=A[0]) == ALIAS
+    assert call(counts=A[1] + 2) == ALIGN

@@ -1,0 +1,232 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+* route: GPU logits within LOGIT_TOL of the fp64 oracle, top-k equal where
+  the choice is unique (near ties audited), counts/offsets bit-exact.
+* integer inputs: exact logits on both sides, so routing (tie-breaks
+  included), slots, rows and the whole chain must match bit for bit.
+* dispatch / fixture / combine: the oracle's routing is handed to the GPU
+  (moe_plan) so both sides start from the same choice; counts, offsets,
+  tok_row, row_src, rows and fp8 scales bit-exact, combine within tolerance.
+Small shapes are checked element by element; the five workload shapes at
+full size on sampled rows and tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_router_gate_amd import inputs as I
+from combine_router_gate_amd import moe
+from oracle import moe_oracle as O
+from _gpu_common import (LOGIT_TOL, check_bf16_close, check_f32_close, note,
+                         to_dev, to_host, topk_audit, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+C = I.CONFIGS
+SMALL = {
+    "tiny": C["tiny"],
+    "mixtral_s": C["mixtral"].with_shape(T=300, H=512),
+    "decode": C["dsv3_decode"],
+    "prefill_s": C["dsv3_prefill"].with_shape(T=333, H=1024),
+    "moonep_s": C["moonep_skew"].with_shape(T=517),
+    "f32_wide": C["tiny"].with_shape(T=130, H=256, E=100, k=4, pad=3),
+    "fp8_routed_f32": C["mixtral"].with_shape(T=70, H=256, E=20, k=3, pad=5,
+                                              payload="fp8"),
+    "f32_to_fp8": C["tiny"].with_shape(T=50, H=128, E=64, k=6, pad=2,
+                                       payload="fp8", y_dtype="bf16",
+                                       expert="scale"),
+    "e512_k16": C["moonep_skew"].with_shape(T=100, H=64, E=512, k=16, pad=8,
+                                            zipf_bias=False),
+    "h8": C["mixtral"].with_shape(T=65, H=8, E=24, k=2, pad=1),
+    "e40_k5": C["dsv3_decode"].with_shape(T=191, H=384, E=40, k=5, pad=16),
+}
+FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
+
+
+def _route_gpu(wl):
+    cfg = wl.cfg
+    x, w = to_dev(wl.x), to_dev(wl.w_gate)
+    b = to_dev(wl.bias) if wl.bias is not None else None
+    return moe.route(x, w, cfg.k, cfg.pad, bias=b, want_logits=True), x
+
+
+def _route_case(name, cfg, seed):
+    note(f"route {name} seed={seed} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    wl = I.make_workload(cfg, seed)
+    p, _ = _route_gpu(wl)
+    torch.cuda.synchronize()
+    o = O.route(wl.x.values, wl.w_gate.values, wl.bias, cfg.k, cfg.pad)
+    gl = to_host(p["logits"])
+    dl = np.abs(gl.astype(np.float64) - o["logits"]).max()
+    assert dl <= LOGIT_TOL, dl
+    gi, gw = to_host(p["topk_idx"]), to_host(p["topk_w"])
+    near = topk_audit(gi, gw, o["logits"], gl, cfg.k)
+    counts, offs = to_host(p["counts"]), to_host(p["offsets"])
+    if (gi == o["topk_idx"]).all():
+        assert np.array_equal(counts, o["counts"])
+        assert np.array_equal(offs, o["offsets"])
+    else:   # a near tie went the other way: the plan must still be valid
+        assert counts.sum() == cfg.T * cfg.k
+        assert np.array_equal(counts, np.bincount(gi.ravel(), minlength=cfg.E))
+        seg = np.diff(offs.astype(np.int64))
+        assert offs[0] == 0 and (seg % cfg.pad == 0).all()
+        assert ((seg >= counts) & (seg - counts < cfg.pad)).all()
+    note(f"route {name}: max|dlogit|={dl:.2e} near-ties={near}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route_small(name):
+    _route_case(name, SMALL[name], 1)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_route_full(name):
+    _route_case(name, C[name], 0)
+
+
+# ------------------------------------------------------------------ integer
+
+INT_CASES = {
+    "int_e8": C["mixtral"].with_shape(T=257, H=256, E=8, k=2, pad=4),
+    "int_e256": C["dsv3_decode"].with_shape(T=200, H=512, E=256, k=8),
+    "int_f32_e20": C["tiny"].with_shape(T=99, H=64, E=20, k=3, pad=2),
+    "int_e384_fp8": C["moonep_skew"].with_shape(T=130, H=256, payload="fp8",
+                                               zipf_bias=False),
+}
+
+
+@pytest.mark.parametrize("name", list(INT_CASES))
+def test_integer_inputs_bit_exact_chain(name):
+    """Integer x and W in {-2..2}: logits are exact integers on both sides,
+    ties are frequent, and the chain from the GPU's own routing must equal
+    the oracle's exactly (combine within tolerance)."""
+    cfg = INT_CASES[name]
+    note(f"integer chain {name}")
+    wl = I.integer_workload(cfg, 3)
+    p, x = _route_gpu(wl)
+    o = O.route(wl.x.values, wl.w_gate.values, None, cfg.k, cfg.pad)
+    assert np.array_equal(to_host(p["logits"]).astype(np.float64), o["logits"])
+    assert np.array_equal(to_host(p["topk_idx"]), o["topk_idx"])
+    np.testing.assert_allclose(to_host(p["topk_w"]), o["topk_w"], rtol=0,
+                               atol=2e-6)
+    assert np.array_equal(to_host(p["counts"]), o["counts"])
+    assert np.array_equal(to_host(p["offsets"]), o["offsets"])
+    _dispatch_combine_compare(wl, o, p, x, full_check=True)
+
+
+# ------------------------------------------------------------------ dispatch
+
+def _oracle_rows(wl, row_src, rows_idx):
+    """Oracle payload (and scales) for the selected rows."""
+    pay, sc = [], []
+    x = wl.x.values
+    for r in rows_idx:
+        p, s = O.dispatch_row(x[row_src[r]], wl.cfg.payload)
+        pay.append(p)
+        sc.append(s)
+    return pay, sc
+
+
+def _dispatch_combine_compare(wl, o, p, x, full_check, sample_rows=1024,
+                              sample_tokens=256):
+    """Given identical routing on both sides (o: oracle route, p: GPU plan),
+    compare dispatch, fixture and combine."""
+    cfg = wl.cfg
+    cap = O.rows_capacity(cfg.T, cfg.E, cfg.k, cfg.pad)
+    o_tok, o_src = O.assign_slots(o["topk_idx"], o["offsets"], cfg.E, cap)
+    d = moe.dispatch(x, p, payload="fp8" if cfg.payload == "fp8" else "same")
+    sigma_d = to_dev(wl.sigma)
+    y = moe.expert_fixture(d, p, sigma_d, y_dtype=torch_dtype(cfg.y_dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(d["tok_row"]), o_tok)
+    assert np.array_equal(to_host(d["row_src"]), o_src)
+
+    valid = np.nonzero(o_src >= 0)[0]
+    rng = np.random.default_rng(0)
+    if full_check or len(valid) <= sample_rows:
+        rsel = valid
+    else:
+        # random rows plus the first and last row of every expert segment
+        firsts = o["offsets"][:-1][o["counts"] > 0]
+        lasts = (o["offsets"][:-1] + o["counts"] - 1)[o["counts"] > 0]
+        rsel = np.unique(np.concatenate(
+            [rng.choice(valid, sample_rows, replace=False), firsts, lasts]))
+    ridx = torch.from_numpy(rsel.astype(np.int64)).cuda()
+    g_rows = to_host(d["rows"][ridx])
+    g_sc = to_host(d["row_scales"][ridx]) if cfg.payload == "fp8" else None
+    g_y = to_host(y[ridx])
+    pay, sc = _oracle_rows(wl, o_src, rsel)
+    for i, r in enumerate(rsel):
+        assert np.array_equal(g_rows[i], pay[i]), f"row {r}"
+        if g_sc is not None:
+            assert np.array_equal(g_sc[i], sc[i]), f"scales of row {r}"
+        e = O.expert_of_row(o["offsets"], r)
+        oy = O.expert_fixture_row(pay[i], sc[i], wl.sigma[e], cfg.payload,
+                                  cfg.y_dtype)
+        assert np.array_equal(g_y[i], oy), f"fixture row {r}"
+
+    # combine, with the oracle's weights on both sides
+    w_d = to_dev(o["topk_w"])
+    shared = to_dev(wl.shared) if wl.shared is not None else None
+    resid = to_dev(wl.residual) if wl.residual is not None else None
+    if resid is not None:
+        res_out, rnr = moe.combine_residual(y, d["tok_row"], w_d, shared, resid)
+    else:
+        out = moe.combine_residual(y, d["tok_row"], w_d, shared, None,
+                                   out_dtype=torch_dtype(cfg.y_dtype))
+    torch.cuda.synchronize()
+    if full_check or cfg.T <= sample_tokens:
+        tsel = np.arange(cfg.T)
+    else:
+        tsel = np.unique(np.concatenate([rng.choice(cfg.T, sample_tokens,
+                                                    replace=False),
+                                         [0, cfg.T - 1]]))
+    tidx = torch.from_numpy(tsel.astype(np.int64)).cuda()
+    x_vals = wl.x.values
+    routed = np.zeros((len(tsel), cfg.H))
+    for i, t in enumerate(tsel):
+        yrows = []
+        for j in range(cfg.k):
+            e = int(o["topk_idx"][t, j])
+            pj, sj = O.dispatch_row(x_vals[t], cfg.payload)
+            yr = O.expert_fixture_row(pj, sj, wl.sigma[e], cfg.payload,
+                                      cfg.y_dtype)
+            yrows.append(yr if cfg.y_dtype == "f32" else O.bf16_value(yr))
+        routed[i] = O.combine_token(np.array(yrows), o["topk_w"][t])
+    if resid is not None:
+        sh = wl.shared.values[tsel] if wl.shared is not None else None
+        o_res, o_rnr, o_exact = O.farskip_update(routed, sh,
+                                                 wl.residual.values[tsel])
+        err = check_bf16_close(to_host(res_out[tidx]), o_exact, what="residual")
+        assert np.array_equal(to_host(rnr[tidx]), o_rnr)
+        note(f"combine max|err| residual={err:.2e}")
+    else:
+        if cfg.y_dtype == "f32":
+            check_f32_close(to_host(out[tidx]), routed, what="routed f32")
+        else:
+            err = check_bf16_close(to_host(out[tidx]), routed, what="routed")
+            note(f"combine max|err| routed={err:.2e}")
+
+
+def _dc_case(name, cfg, seed, full_check):
+    note(f"dispatch/combine {name} seed={seed} T={cfg.T} H={cfg.H} E={cfg.E} "
+         f"k={cfg.k} payload={cfg.payload}")
+    wl = I.make_workload(cfg, seed)
+    o = O.route(wl.x.values, wl.w_gate.values, wl.bias, cfg.k, cfg.pad)
+    idx_d = to_dev(o["topk_idx"])
+    p = moe.plan(idx_d, cfg.E, cfg.pad)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(p["counts"]), o["counts"])
+    assert np.array_equal(to_host(p["offsets"]), o["offsets"])
+    x = to_dev(wl.x)
+    _dispatch_combine_compare(wl, o, p, x, full_check)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dispatch_combine_small(name):
+    _dc_case(name, SMALL[name], 2, full_check=True)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_dispatch_combine_full(name):
+    _dc_case(name, C[name], 0, full_check=False)
