@@ -12,35 +12,53 @@
 // so the auxiliary stream never depends on the routed combine.
 //
 // Design for CDNA4: one wavefront per token.  Lanes 0..k-1 fetch the k
-// (row, weight) pairs, broadcast to scalar registers; each lane then owns 8
-// consecutive hidden elements per step, issues all k 16-byte row gathers
-// plus the residual and shared loads before any arithmetic (up to 10
-// independent 16-byte loads in flight per lane), accumulates in fp32 with
-// j ascending (fmaf), adds shared then residual, and rounds once to bf16
-// with the hardware converter.  No floating-point atomics: every output
-// element is produced by exactly one lane.
+// (row, weight) pairs, broadcast to scalar registers; each lane then owns
+// two groups of 8 consecutive hidden elements per step and issues all their
+// 16-byte row gathers plus the residual and shared loads before any
+// arithmetic (20 independent loads in flight per lane at k = 8),
+// accumulates in fp32 with j ascending (fmaf), adds shared then residual,
+// rounds once to bf16 with the hardware converter and writes with streaming
+// stores.  No floating-point atomics: every output element is produced by
+// exactly one lane.  In-place use (residual_out == residual_in) is safe:
+// each element is read before the same lane overwrites it.
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-template <int YT>  // 0 = fp32 rows, 1 = bf16 rows
-__device__ __forceinline__ void load8(const unsigned char* __restrict__ base,
-                                      int c, float f[8]) {
+// 8 consecutive elements of a row: one 16-byte vector of bf16 or two of fp32
+template <int YT> struct Chunk8;
+template <> struct Chunk8<1> { u32x4 a; };
+template <> struct Chunk8<0> { u32x4 a, b; };
+
+template <int YT>
+__device__ __forceinline__ Chunk8<YT> load8(const unsigned char* __restrict__ row,
+                                            int c) {
+  Chunk8<YT> v;
   if constexpr (YT == 1) {
-    unpack8_bf16(ld16_stream(base + (size_t)c * 16), f);
+    v.a = ld16_stream(row + (size_t)c * 16);
   } else {
-    const u32x4 v0 = ld16_stream(base + (size_t)c * 32);
-    const u32x4 v1 = ld16_stream(base + (size_t)c * 32 + 16);
+    v.a = ld16_stream(row + (size_t)c * 32);
+    v.b = ld16_stream(row + (size_t)c * 32 + 16);
+  }
+  return v;
+}
+template <int YT>
+__device__ __forceinline__ void unpack8(const Chunk8<YT>& v, float f[8]) {
+  if constexpr (YT == 1) {
+    unpack8_bf16(v.a, f);
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[i] = __uint_as_float(v0[i]);
-      f[4 + i] = __uint_as_float(v1[i]);
+      f[i] = __uint_as_float(v.a[i]);
+      f[4 + i] = __uint_as_float(v.b[i]);
     }
   }
 }
 
-// OUT: 0 = dual residual (bf16), 1 = routed-only bf16, 2 = routed-only fp32
+// OUT: 0 = dual residual (bf16), 1 = routed-only bf16, 2 = routed-only fp32.
+// Each lane keeps U = 2 groups of 8 elements in flight: for k = 8 that is
+// 2 * (8 gathers + shared + residual) 16-byte loads issued before any math.
 template <int KMAX, int YT, int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const unsigned char* __restrict__ y, long long y_rows, int H,
@@ -48,6 +66,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     int T, int k, const unsigned char* __restrict__ shared,
     const unsigned char* res_in, unsigned char* res_out,
     unsigned char* __restrict__ rnr, unsigned char* __restrict__ out) {
+  constexpr int U = 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
@@ -72,55 +91,65 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const size_t yrowb = (size_t)H * (YT == 1 ? 2 : 4);
   const size_t trow = (size_t)t * H * 2;     // byte offset of token row, bf16
   const int nc8 = H / 8;
-  for (int c = lane; c < nc8; c += 64) {
-    float g[KMAX][8];
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int c0 = lane; c0 < nc8; c0 += 64 * U) {
+    Chunk8<YT> g[U][KMAX];
+    u32x4 shv[U], rsv[U];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (rj[j] >= 0) load8<YT>(y + (size_t)rj[j] * yrowb, c, g[j]);
-    }
-    float sh[8], rs[8];
-    if (shared != nullptr) {
-      unpack8_bf16(ld16_stream(shared + trow + (size_t)c * 16), sh);
-    } else {
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64;
+      if (c < nc8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sh[i] = 0.0f;
-    }
-    if constexpr (OUT == 0) unpack8_bf16(ld16(res_in + trow + (size_t)c * 16), rs);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (rj[j] >= 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], g[j][i], acc[i]);
+        for (int j = 0; j < KMAX; ++j)
+          if (rj[j] >= 0) g[u][j] = load8<YT>(y + (size_t)rj[j] * yrowb, c);
+        shv[u] = shared != nullptr ? ld16_stream(shared + trow + (size_t)c * 16) : z;
+        if constexpr (OUT == 0) rsv[u] = ld16(res_in + trow + (size_t)c * 16);
       }
     }
-    if constexpr (OUT == 0) {
-      float o[8], a[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o[i] = (acc[i] + sh[i]) + rs[i];
-        a[i] = rs[i] + sh[i];
-      }
-      st16(res_out + trow + (size_t)c * 16, pack8_bf16(o));
-      st16(rnr + trow + (size_t)c * 16, pack8_bf16(a));
-    } else {
-      float o[8];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64;
+      if (c >= nc8) continue;
+      float acc[8], sh[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = acc[i] + sh[i];
-      if constexpr (OUT == 1) {
-        st16(out + trow + (size_t)c * 16, pack8_bf16(o));
-      } else {
-        u32x4 v0, v1;
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v0[i] = __float_as_uint(o[i]);
-          v1[i] = __float_as_uint(o[4 + i]);
+      for (int j = 0; j < KMAX; ++j) {
+        if (rj[j] >= 0) {
+          float f[8];
+          unpack8<YT>(g[u][j], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], f[i], acc[i]);
         }
-        unsigned char* p = out + (size_t)t * H * 4 + (size_t)c * 32;
-        st16(p, v0);
-        st16(p + 16, v1);
+      }
+      unpack8_bf16(shv[u], sh);
+      if constexpr (OUT == 0) {
+        float rs[8], o[8], a[8];
+        unpack8_bf16(rsv[u], rs);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          o[i] = (acc[i] + sh[i]) + rs[i];
+          a[i] = rs[i] + sh[i];
+        }
+        st16_stream(res_out + trow + (size_t)c * 16, pack8_bf16(o));
+        st16_stream(rnr + trow + (size_t)c * 16, pack8_bf16(a));
+      } else {
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = acc[i] + sh[i];
+        if constexpr (OUT == 1) {
+          st16_stream(out + trow + (size_t)c * 16, pack8_bf16(o));
+        } else {
+          u32x4 v0, v1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v0[i] = __float_as_uint(o[i]);
+            v1[i] = __float_as_uint(o[4 + i]);
+          }
+          unsigned char* p = out + (size_t)t * H * 4 + (size_t)c * 32;
+          st16_stream(p, v0);
+          st16_stream(p + 16, v1);
+        }
       }
     }
   }
