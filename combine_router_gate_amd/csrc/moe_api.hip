@@ -131,14 +131,10 @@ int moe_route(const void* x, int x_dtype, int T, int H, const void* w_gate,
   if (trace_on())
     std::fprintf(stderr, "moe_route T=%d H=%d E=%d k=%d pad=%d dtype=%d\n", T,
                  H, E, k, pad, x_dtype);
-  hipStream_t s = (hipStream_t)stream;
-  if (T > 0) {
-    st = hip_status(moe::launch_gate_topk(x, w_gate, x_dtype, bias, T, H, E, k,
-                                          topk_idx, topk_w, logits_dbg, s));
-    if (st != MOE_OK) return st;
-  }
-  return hip_status(
-      moe::launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s));
+  return hip_status(moe::launch_route(x, w_gate, x_dtype, bias, T, H, E, k,
+                                      pad, topk_idx, topk_w, counts, offsets,
+                                      logits_dbg, workspace,
+                                      (hipStream_t)stream));
 }
 
 int moe_plan(const int32_t* topk_idx, int T, int k, int E, int pad,

@@ -98,6 +98,17 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
+// ------------------------------------------------------------------ barrier
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations
+// complete, then s_barrier.  __syncthreads() also waits for every
+// outstanding global load of the wave (its fence semantics), which would
+// drain a software-pipelined prefetch at each step; this one keeps them in
+// flight.  Only valid where the barrier orders LDS accesses alone.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------------------ keys
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).

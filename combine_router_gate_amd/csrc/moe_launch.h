@@ -30,10 +30,12 @@ inline size_t workspace_bytes(int T, int E, int k) {
 // dtype codes of moe.h
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
-hipError_t launch_gate_topk(const void* x, const void* w, int xdt,
-                            const float* bias, int T, int H, int E, int k,
-                            int32_t* topk_idx, float* topk_w,
-                            float* logits_dbg, hipStream_t s);
+// gate + top-k + tile histogram + scan (the whole of moe_route)
+hipError_t launch_route(const void* x, const void* w, int xdt,
+                        const float* bias, int T, int H, int E, int k,
+                        int pad, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* offsets, float* logits_dbg,
+                        void* workspace, hipStream_t s);
 
 hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
                        int32_t* counts, int32_t* offsets, void* workspace,

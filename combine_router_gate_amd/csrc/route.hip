@@ -91,6 +91,65 @@ __device__ __forceinline__ f32x4 mfma_step(const Frag<float>& a,
 
 // ------------------------------------------------------------------ top-k
 
+// Top-k of one token per 16-lane group.  Lane c of the group holds the
+// logits of experts 16*et + c in v[et] (bias already added).  k rounds of a
+// 16-lane max over 64-bit keys (order-preserving logit key, then inverted
+// expert id) pick the largest logit, lowest index first on ties.  Lane j of
+// the group writes the j-th choice and its renormalised weight.
+template <int ET>
+__device__ __forceinline__ void topk_select_write(
+    const float (&v)[ET], int t, int T, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    unsigned long long* tile_bits = nullptr, int* tile_sel = nullptr,
+    int tl = 0) {
+  const int c = threadIdx.x & 15;
+  uint32_t taken = 0;
+  int sel_e[MOE_MAX_TOPK];
+  float sel_v[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    sel_e[j] = 0;
+    sel_v[j] = 0.0f;
+    if (j < k) {
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const int e = et * 16 + c;
+        const unsigned long long key =
+            ((unsigned long long)f32_order_key(v[et]) << 32) |
+            (unsigned long long)(0xffffffffu - (uint32_t)e);
+        const bool ok = e < E && !((taken >> et) & 1u);
+        best = (ok && key > best) ? key : best;
+      }
+      best = max16_u64(best);
+      const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+      if ((ew & 15) == c) taken |= 1u << (ew >> 4);
+      sel_e[j] = ew;
+      sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
+    }
+  }
+  float ex[MOE_MAX_TOPK];
+  float den = 0.0f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    ex[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.0f;
+    den += ex[j];
+  }
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && c == j) {
+        topk_idx[(size_t)t * k + j] = sel_e[j];
+        topk_w[(size_t)t * k + j] = ex[j] / den;
+        if (tile_bits != nullptr) {
+          atomicOr(&tile_bits[sel_e[j]], 1ull << tl);
+          tile_sel[tl * MOE_MAX_TOPK + j] = sel_e[j];
+        }
+      }
+    }
+  }
+}
+
 // acc[et][i] holds the logit of token t0 + 4*(lane/16) + i and expert
 // 16*et + lane%16 (the 16x16 MFMA output layout).
 template <int ET>
@@ -117,47 +176,7 @@ __device__ __forceinline__ void topk_epilogue(
       if (logits_dbg != nullptr && t < T && e < E)
         logits_dbg[(size_t)t * E + e] = v[et];
     }
-    uint32_t taken = 0;
-    int sel_e[MOE_MAX_TOPK];
-    float sel_v[MOE_MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      sel_e[j] = 0;
-      sel_v[j] = 0.0f;
-      if (j < k) {
-        unsigned long long best = 0ull;
-#pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          const int e = et * 16 + c;
-          const unsigned long long key =
-              ((unsigned long long)f32_order_key(v[et]) << 32) |
-              (unsigned long long)(0xffffffffu - (uint32_t)e);
-          const bool ok = e < E && !((taken >> et) & 1u);
-          best = (ok && key > best) ? key : best;
-        }
-        best = max16_u64(best);
-        const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-        if ((ew & 15) == c) taken |= 1u << (ew >> 4);
-        sel_e[j] = ew;
-        sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
-      }
-    }
-    float ex[MOE_MAX_TOPK];
-    float den = 0.0f;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      ex[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.0f;
-      den += ex[j];
-    }
-    if (t < T) {
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        if (j < k && c == j) {
-          topk_idx[(size_t)t * k + j] = sel_e[j];
-          topk_w[(size_t)t * k + j] = ex[j] / den;
-        }
-      }
-    }
+    topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w);
   }
 }
 
@@ -217,13 +236,13 @@ __global__ __launch_bounds__(256) void gate_topk_wide_kernel(
   load_w(0);
   load_a(0);
   for (int ch = 0; ch < nchunks; ++ch) {
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
       const int p = tid + 256 * i;
       st16(wlds + (p >> 3) * ROWB + (p & 7) * 16, wreg[i]);
     }
-    __syncthreads();
+    lds_barrier();
     Frag<XT> acur[KSTEPS];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) acur[s] = anext[s];
@@ -249,6 +268,177 @@ __global__ __launch_bounds__(256) void gate_topk_wide_kernel(
     }
   }
   topk_epilogue<ET>(acc, t0, T, E, k, bias, topk_idx, topk_w, logits_dbg);
+}
+
+// ------------------------------------------------------------------ gate v2, bf16, E >= 64
+
+// One workgroup = 4 waves = 64 tokens.  Wave w owns all 64 tokens and the
+// EPW expert tiles [w*EPW, (w+1)*EPW) (16 experts each), i.e. a 64 x 16*EPW
+// block of logits in 4*EPW MFMA accumulators, so each x fragment read from
+// LDS feeds EPW MFMAs and each gate-weight fragment feeds 4.
+//
+// The hidden dimension advances in super-steps of 128: lane group g =
+// lane/16 owns k in [K0 + 32g, K0 + 32g + 32) as four 8-element pieces, one
+// per 16x16x32 MFMA; x and W use the same (g, piece) -> k map, so each lane
+// reads 64 contiguous bytes of every row it touches.
+//  * x: the workgroup loads the [64 tokens x 128 k] tile (16 KB, 64 B per
+//    thread, non-temporal) D super-steps ahead into a register ring and
+//    stores it into one of two LDS slots right before use.  Within a slot,
+//    16-byte piece p of row r sits at position p ^ (r & 15), so the 16 rows
+//    read by an MFMA operand fall into distinct banks.
+//  * W: each wave loads its own B fragments from global memory (the gate
+//    weight stays L2-resident while x streams past it) into a D-deep
+//    register ring.
+// Every load in the pipeline is unconditional and unmasked (addresses
+// clamped into the arrays), so the compiler counts outstanding loads exactly
+// instead of draining them; out-of-range x (a token past T or k >= H) is
+// zeroed only when the tile is written to LDS, after the load has landed.
+// Out-of-range W then multiplies zeros (k >= H) or belongs to a padded
+// expert that the top-k ignores.  One LDS-only barrier per super-step.
+// Afterwards the logits go through LDS so each 16-lane group sees all
+// experts of one token for the top-k, and the tile's expert bitmaps give
+// its histogram and slot ranks.
+template <int EPW, int PQ, int D>
+__global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int T, int H, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits_dbg, int32_t* __restrict__ tile_base,
+    int32_t* __restrict__ slot_rank) {
+  constexpr int ET = 4 * EPW;              // expert tiles of the workgroup
+  constexpr int EP = 16 * ET;              // padded experts
+  constexpr int LROW = EP + 4;             // logits row stride (floats)
+  constexpr int KS = 32 * PQ;              // k per super-step
+  constexpr int RB = 2 * KS;               // bytes of one x row per step
+  constexpr int NP = 4 * PQ;               // 16-byte pieces per row
+  constexpr int XSLOT = 64 * RB;           // bytes of one x slot
+  constexpr int LDS_BYTES = (64 * LROW * 4 > 2 * XSLOT) ? 64 * LROW * 4 : 2 * XSLOT;
+  __shared__ __align__(16) unsigned char lds[LDS_BYTES];
+  __shared__ unsigned long long tile_bits[EP];     // token bitmap per expert
+  __shared__ int tile_sel[64 * MOE_MAX_TOPK];      // chosen experts
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * 64;
+  const int nss = (H + KS - 1) / KS;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int e = tid; e < EP; e += 256) tile_bits[e] = 0ull;
+
+  // x tile loader: thread covers row tid/4, pieces PQ*(tid%4) .. +PQ-1
+  const int xr = tid >> 2, xp = (tid & 3) * PQ;
+  const bool xrow_ok = t0 + xr < T;
+  const uint16_t* xrow = x + (size_t)(xrow_ok ? t0 + xr : T - 1) * H;
+  const uint16_t* wrow[EPW];
+#pragma unroll
+  for (int et = 0; et < EPW; ++et) {
+    const int e = (wv * EPW + et) * 16 + c16;
+    wrow[et] = w + (size_t)(e < E ? e : E - 1) * H;
+  }
+
+  u32x4 xreg[D][PQ];
+  u32x4 wreg[D][EPW][PQ];
+  auto load_x = [&](int i, u32x4 (&dst)[PQ]) {
+#pragma unroll
+    for (int q = 0; q < PQ; ++q) {
+      const int kk = i * KS + (xp + q) * 8;
+      dst[q] = ld16_stream(xrow + (kk < H ? kk : H - 8));
+    }
+  };
+  auto load_w = [&](int i, u32x4 (&dst)[EPW][PQ]) {
+#pragma unroll
+    for (int et = 0; et < EPW; ++et)
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+        const int kk = i * KS + g * (8 * PQ) + q * 8;
+        dst[et][q] = ld16(wrow[et] + (kk < H ? kk : H - 8));
+      }
+  };
+
+  f32x4 acc[4][EPW];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_x(j, xreg[j]);
+    load_w(j, wreg[j]);
+  }
+
+  // steps past the end (up to D-1 when nss % D != 0) multiply zeros
+  for (int i0 = 0; i0 < nss; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      unsigned char* slot = lds + (i & 1) * XSLOT;
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+        const bool ok = xrow_ok && i * KS + (xp + q) * 8 < H;
+        st16(slot + xr * RB + (((xp + q) ^ (xr & (NP - 1))) * 16),
+             ok ? xreg[j][q] : z);
+      }
+      lds_barrier();
+      load_x(i + D, xreg[j]);
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int r = tt * 16 + c16;
+          const int p = g * PQ + q;
+          Frag<uint16_t> a;
+          a.v = *reinterpret_cast<const u32x4*>(slot + r * RB + ((p ^ (r & (NP - 1))) * 16));
+#pragma unroll
+          for (int et = 0; et < EPW; ++et) {
+            Frag<uint16_t> b;
+            b.v = wreg[j][et][q];
+            acc[tt][et] = mfma_step(a, b, acc[tt][et]);
+          }
+        }
+      }
+      load_w(i + D, wreg[j]);
+    }
+  }
+
+  // logits -> LDS [64 tokens][LROW] (bias added), then top-k per token
+  __syncthreads();
+  float* lg = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) {
+      const int e = (wv * EPW + et) * 16 + c16;
+      const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[(tt * 16 + g * 4 + i) * LROW + e] = acc[tt][et][i] + b;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int tl = wv * 16 + pass * 4 + g;
+    const int t = t0 + tl;
+    float v[ET];
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      const int e = et * 16 + c16;
+      v[et] = lg[tl * LROW + e];
+      if (logits_dbg != nullptr && t < T && e < E)
+        logits_dbg[(size_t)t * E + e] = v[et];
+    }
+    topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w, tile_bits,
+                          tile_sel, tl);
+  }
+  // the tile's histogram and slot ranks (as tile_histogram_kernel does)
+  __syncthreads();
+  for (int e = tid; e < E; e += 256)
+    tile_base[(size_t)blockIdx.x * E + e] = __popcll(tile_bits[e]);
+  const int n = min(64, T - t0) * k;
+  for (int q = tid; q < n; q += 256) {
+    const int tl = q / k, j = q - tl * k;
+    const int e = tile_sel[tl * MOE_MAX_TOPK + j];
+    slot_rank[(size_t)t0 * k + q] = __popcll(tile_bits[e] & ((1ull << tl) - 1ull));
+  }
 }
 
 // ------------------------------------------------------------------ gate, E < 64
@@ -353,13 +543,15 @@ __global__ __launch_bounds__(256) void tile_histogram_kernel(
 // ------------------------------------------------------------------ scan
 
 // Single workgroup of 1024 threads.  Thread (p, e) with p < parts owns a
-// contiguous run of tiles of expert e.  Pass 1 sums the runs, the LDS scans
-// give each run's start within its expert and the padded expert offsets,
-// pass 2 overwrites every tile count with the first row of that
-// (tile, expert) run: offsets[e] + tokens of e in earlier tiles.
+// contiguous run of tiles of expert e.  Pass 1 sums the runs (32 loads in
+// flight per thread), an LDS pass and a shuffle scan give each run's start
+// and the padded expert offsets, pass 2 overwrites every tile count with the
+// first row of that (tile, expert) run: offsets[e] + tokens of e in earlier
+// tiles.  Runs of up to 32 tiles stay in registers between the passes.
 __global__ __launch_bounds__(1024) void expert_scan_kernel(
     int32_t* __restrict__ tile_base, int ntiles, int E, int pad,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  constexpr int B = 32;
   __shared__ int part[1024];
   __shared__ int scan[1024];
   const int tid = threadIdx.x;
@@ -370,17 +562,14 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
   const int lo = active ? (int)((long long)p * ntiles / parts) : 0;
   const int hi = active ? (int)((long long)(p + 1) * ntiles / parts) : 0;
 
+  int v[B];
   int sum = 0;
-  {
-    int tl = lo;
-    for (; tl + 8 <= hi; tl += 8) {
-      int v[8];
+  for (int b0 = lo; b0 < hi; b0 += B) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = tile_base[(size_t)(tl + u) * E + e];
+    for (int u = 0; u < B; ++u)
+      v[u] = (b0 + u < hi) ? tile_base[(size_t)(b0 + u) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
-    }
-    for (; tl < hi; ++tl) sum += tile_base[(size_t)tl * E + e];
+    for (int u = 0; u < B; ++u) sum += v[u];
   }
   if (active) part[p * E + e] = sum;
   __syncthreads();
@@ -388,30 +577,47 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
   if (tid < E) {
     int run = 0;
     for (int q = 0; q < parts; ++q) {
-      const int v = part[q * E + tid];
+      const int c = part[q * E + tid];
       part[q * E + tid] = run;
-      run += v;
+      run += c;
     }
     counts[tid] = run;
     padded = (run + pad - 1) / pad * pad;
   }
-  scan[tid] = padded;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  // inclusive scan of the padded counts: within each wave by shuffles,
+  // then across the 16 wave totals
+  const int ln = tid & 63, wid = tid >> 6;
+  int incl = padded;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (ln >= off) incl += o;
   }
+  __shared__ int wsum[16];
+  if (ln == 63) wsum[wid] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int q = 0; q < wid; ++q) before += wsum[q];
+  scan[tid] = incl + before;
+  __syncthreads();
   if (tid < E) offsets[tid + 1] = scan[tid];
   if (tid == 0) offsets[0] = 0;
   if (active) {
     int run = part[p * E + e] + (e == 0 ? 0 : scan[e - 1]);
-    for (int tl = lo; tl < hi; ++tl) {
-      const size_t i = (size_t)tl * E + e;
-      const int c = tile_base[i];
-      tile_base[i] = run;
-      run += c;
+    const bool kept = hi - lo <= B;     // the single batch is still in v
+    for (int b0 = lo; b0 < hi; b0 += B) {
+      if (!kept) {
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          v[u] = (b0 + u < hi) ? tile_base[(size_t)(b0 + u) * E + e] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (b0 + u < hi) {
+          tile_base[(size_t)(b0 + u) * E + e] = run;
+          run += v[u];
+        }
+      }
     }
   }
 }
@@ -421,7 +627,10 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
 template <typename XT>
 static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
                                     int T, int H, int E, int k, int32_t* idx,
-                                    float* tw, float* dbg, hipStream_t s) {
+                                    float* tw, float* dbg, int32_t* tb,
+                                    int32_t* sr, bool* fused_hist,
+                                    hipStream_t s) {
+  *fused_hist = false;
   const int et = (E + 15) / 16;
   if (et <= 2) {
     const dim3 grid((T + 15) / 16);
@@ -434,6 +643,19 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     return hipGetLastError();
   }
   const dim3 grid((T + 63) / 64);
+  if constexpr (sizeof(XT) == 2) {
+#define MOE_GATE_V2(EPWV, PQV, DV)                                         \
+  hipLaunchKernelGGL((gate_topk_v2_kernel<EPWV, PQV, DV>), grid, dim3(256), \
+                     0, s, x, w, bias, T, H, E, k, idx, tw, dbg, tb, sr)
+    if (et <= 4) MOE_GATE_V2(1, 2, 4);
+    else if (et <= 8) MOE_GATE_V2(2, 2, 4);
+    else if (et <= 16) MOE_GATE_V2(4, 2, 4);
+    else if (et <= 24) MOE_GATE_V2(6, 2, 3);
+    else MOE_GATE_V2(8, 2, 2);
+#undef MOE_GATE_V2
+    *fused_hist = true;
+    return hipGetLastError();
+  }
 #define MOE_GATE_WIDE(ETV)                                                    \
   hipLaunchKernelGGL((gate_topk_wide_kernel<XT, ETV>), grid, dim3(256), 0, s, \
                      x, w, bias, T, H, E, k, idx, tw, dbg)
@@ -446,16 +668,43 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   return hipGetLastError();
 }
 
-hipError_t launch_gate_topk(const void* x, const void* w, int xdt,
-                            const float* bias, int T, int H, int E, int k,
-                            int32_t* topk_idx, float* topk_w,
-                            float* logits_dbg, hipStream_t s) {
+hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
+                       int32_t* counts, int32_t* offsets, void* workspace,
+                       hipStream_t s);
+
+static hipError_t launch_scan(int32_t* tile_base, int nt, int E, int pad,
+                              int32_t* counts, int32_t* offsets,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, s, tile_base,
+                     nt, E, pad, counts, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const void* x, const void* w, int xdt,
+                        const float* bias, int T, int H, int E, int k,
+                        int pad, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* offsets, float* logits_dbg,
+                        void* workspace, hipStream_t s) {
+  if (T == 0)
+    return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
+  int32_t* tile_base = (int32_t*)workspace;
+  int32_t* slot_rank =
+      (int32_t*)((unsigned char*)workspace + ws_tile_bytes(T, E));
+  bool fused = false;
+  hipError_t err;
   if (xdt == DT_BF16)
-    return launch_gate_typed<uint16_t>((const uint16_t*)x, (const uint16_t*)w,
-                                       bias, T, H, E, k, topk_idx, topk_w,
-                                       logits_dbg, s);
-  return launch_gate_typed<float>((const float*)x, (const float*)w, bias, T, H,
-                                  E, k, topk_idx, topk_w, logits_dbg, s);
+    err = launch_gate_typed<uint16_t>((const uint16_t*)x, (const uint16_t*)w,
+                                      bias, T, H, E, k, topk_idx, topk_w,
+                                      logits_dbg, tile_base, slot_rank,
+                                      &fused, s);
+  else
+    err = launch_gate_typed<float>((const float*)x, (const float*)w, bias, T,
+                                   H, E, k, topk_idx, topk_w, logits_dbg,
+                                   tile_base, slot_rank, &fused, s);
+  if (err != hipSuccess) return err;
+  if (!fused)
+    return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
+  return launch_scan(tile_base, num_tiles(T), E, pad, counts, offsets, s);
 }
 
 hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
@@ -471,9 +720,7 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, s, tile_base,
-                     nt, E, pad, counts, offsets);
-  return hipGetLastError();
+  return launch_scan(tile_base, nt, E, pad, counts, offsets, s);
 }
 
 }  // namespace moe

@@ -39,6 +39,8 @@ SMALL = {
                                             zipf_bias=False),
     "h8": C["mixtral"].with_shape(T=65, H=8, E=24, k=2, pad=1),
     "e40_k5": C["dsv3_decode"].with_shape(T=191, H=384, E=40, k=5, pad=16),
+    "bf16_e100_h320": C["mixtral"].with_shape(T=130, H=320, E=100, k=4, pad=7),
+    "bf16_e64_h200": C["mixtral"].with_shape(T=77, H=200, E=64, k=3, pad=2),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 
