@@ -122,18 +122,25 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
 
 // ------------------------------------------------------------------ reductions
 
-// Maximum over each aligned group of 16 lanes (all lanes get the result).
-__device__ __forceinline__ unsigned long long max16_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    const unsigned long long o = __shfl_xor(v, m, 16);
-    v = o > v ? o : v;
-  }
-  return v;
+// 64-bit DPP move within each row of 16 lanes (CTRL: a DPP control word).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf,
+                                             0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(
+      0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
-__device__ __forceinline__ float max16_f32(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+
+// Maximum over each aligned group of 16 lanes (all lanes get the result):
+// rotations by 8, 4, 2, 1 within the DPP row (row_ror = 0x120 + n), so the
+// reduction stays in the ALU instead of round-tripping through LDS.
+__device__ __forceinline__ unsigned long long max16_u64(unsigned long long v) {
+  unsigned long long o;
+  o = dpp_u64<0x128>(v); v = o > v ? o : v;
+  o = dpp_u64<0x124>(v); v = o > v ? o : v;
+  o = dpp_u64<0x122>(v); v = o > v ? o : v;
+  o = dpp_u64<0x121>(v); v = o > v ? o : v;
   return v;
 }
 

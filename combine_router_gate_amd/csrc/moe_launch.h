@@ -11,20 +11,42 @@ namespace moe {
 // Histogram tiles of the workspace for T tokens.
 inline int num_tiles(int T) { return (T + 63) / 64; }
 
-// Workspace layout (int32 arrays, each 256-byte aligned):
-//   tile_base [ntiles, E]  per-tile expert counts, then (after the scan)
-//                          the first row of each tile's tokens for expert e
-//   slot_rank [T, k]       rank of slot (t, j) among its tile's tokens that
-//                          chose the same expert
+// Workspace layout (each array 256-byte aligned):
+//   tile_base [ntiles, E] int32  per-tile expert counts, then (after the
+//                                scan) the first row of each tile's tokens
+//                                for expert e
+//   slot_rank [T, k] int32       rank of slot (t, j) among its tile's tokens
+//                                that chose the same expert
+//   partial   [S, T, EP] fp32    partial gate logits when the hidden
+//                                dimension is split S ways (few tokens);
+//                                S * T <= kSplitRows, EP = experts padded to
+//                                the gate kernel's 64 * EPW
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+constexpr int kSplitRows = 16384;
+constexpr int kSplitMax = 64;
+inline int gate_epw(int E) {           // expert tiles per wave of the gate
+  const int et = (E + 15) / 16;
+  return et <= 4 ? 1 : et <= 8 ? 2 : et <= 16 ? 4 : et <= 24 ? 6 : 8;
+}
+inline int split_max(int T) {          // largest split of H for T tokens
+  if (T <= 0 || T > 2 * kSplitRows) return 1;
+  const int s = 2 * kSplitRows / T;
+  return s < kSplitMax ? s : kSplitMax;
+}
 inline size_t ws_tile_bytes(int T, int E) {
   return align256(size_t(num_tiles(T)) * size_t(E) * 4);
 }
 inline size_t ws_rank_bytes(int T, int k) {
   return align256(size_t(T) * size_t(k) * 4);
 }
+inline size_t ws_partial_bytes(int T, int E) {
+  const int s = split_max(T);
+  return s > 1 ? align256(size_t(s) * T * 64 * gate_epw(E) * 4) : 0;
+}
 inline size_t workspace_bytes(int T, int E, int k) {
-  return T == 0 ? 0 : ws_tile_bytes(T, E) + ws_rank_bytes(T, k);
+  return T == 0 ? 0
+                : ws_tile_bytes(T, E) + ws_rank_bytes(T, k) +
+                      ws_partial_bytes(T, E);
 }
 
 // dtype codes of moe.h

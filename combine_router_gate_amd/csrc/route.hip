@@ -92,10 +92,13 @@ __device__ __forceinline__ f32x4 mfma_step(const Frag<float>& a,
 // ------------------------------------------------------------------ top-k
 
 // Top-k of one token per 16-lane group.  Lane c of the group holds the
-// logits of experts 16*et + c in v[et] (bias already added).  k rounds of a
-// 16-lane max over 64-bit keys (order-preserving logit key, then inverted
-// expert id) pick the largest logit, lowest index first on ties.  Lane j of
-// the group writes the j-th choice and its renormalised weight.
+// logits of experts 16*et + c in v[et] (bias already added).  Each logit
+// becomes a 64-bit key (order-preserving logit key, then inverted expert
+// id), built once; padded experts get key 0.  k rounds of a 16-lane max
+// pick the largest logit, lowest index first on ties; the winner is removed
+// by clearing its high word, which leaves it below every real key (the key
+// of any non-NaN logit has a non-zero high word).  Lane j of the group
+// writes the j-th choice and its renormalised weight.
 template <int ET>
 __device__ __forceinline__ void topk_select_write(
     const float (&v)[ET], int t, int T, int E, int k,
@@ -103,7 +106,13 @@ __device__ __forceinline__ void topk_select_write(
     unsigned long long* tile_bits = nullptr, int* tile_sel = nullptr,
     int tl = 0) {
   const int c = threadIdx.x & 15;
-  uint32_t taken = 0;
+  unsigned long long key[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et) {
+    const int e = et * 16 + c;
+    const uint32_t hi = e < E ? f32_order_key(v[et]) : 0u;
+    key[et] = ((unsigned long long)hi << 32) | (0xffffffffu - (uint32_t)e);
+  }
   int sel_e[MOE_MAX_TOPK];
   float sel_v[MOE_MAX_TOPK];
 #pragma unroll
@@ -111,20 +120,15 @@ __device__ __forceinline__ void topk_select_write(
     sel_e[j] = 0;
     sel_v[j] = 0.0f;
     if (j < k) {
-      unsigned long long best = 0ull;
+      unsigned long long best = key[0];
 #pragma unroll
-      for (int et = 0; et < ET; ++et) {
-        const int e = et * 16 + c;
-        const unsigned long long key =
-            ((unsigned long long)f32_order_key(v[et]) << 32) |
-            (unsigned long long)(0xffffffffu - (uint32_t)e);
-        const bool ok = e < E && !((taken >> et) & 1u);
-        best = (ok && key > best) ? key : best;
-      }
+      for (int et = 1; et < ET; ++et) best = key[et] > best ? key[et] : best;
       best = max16_u64(best);
-      const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-      if ((ew & 15) == c) taken |= 1u << (ew >> 4);
-      sel_e[j] = ew;
+      const uint32_t blo = (uint32_t)best;
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+        if ((uint32_t)key[et] == blo) key[et] &= 0xffffffffull;
+      sel_e[j] = (int)(0xffffffffu - blo);
       sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
     }
   }
@@ -441,6 +445,220 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
   }
 }
 
+// ------------------------------------------------------------------ gate, split over H
+
+// Partial logits over one range of the hidden dimension, for shapes where
+// one workgroup per 64-token tile cannot fill the chip (few tokens): the
+// grid is (token tiles of 16*TT, hidden ranges of KR), each workgroup runs
+// the same pipeline as gate_topk_v2_kernel over [k_lo, k_lo + KR) and
+// writes its fp32 partial logits partial[ks][t][e] (row stride 64*EPW).
+// gate_reduce_topk_kernel adds the ranges in ascending order.
+template <int EPW, int TT, int PQ, int D>
+__global__ __launch_bounds__(256, 1) void gate_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
+    int H, int E, int KR, float* __restrict__ partial) {
+  constexpr int EP = 64 * EPW;             // padded experts
+  constexpr int TTOK = 16 * TT;            // tokens of the workgroup
+  constexpr int KS = 32 * PQ;              // k per super-step
+  constexpr int RB = 2 * KS;               // bytes of one x row per step
+  constexpr int NP = 4 * PQ;               // 16-byte pieces per row
+  constexpr int XSLOT = TTOK * RB;         // bytes of one x slot
+  constexpr int XPT = TTOK * NP / 256;     // x pieces per thread per step
+  static_assert(XPT >= 1 && TTOK * NP % 256 == 0, "tile too small");
+  __shared__ __align__(16) unsigned char lds[2 * XSLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * TTOK;
+  const int ks = blockIdx.y;
+  const int k_lo = ks * KR;
+  const int k_hi = min(H, k_lo + KR);
+  const int nss = (k_hi - k_lo + KS - 1) / KS;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+
+  int xr[XPT], xp[XPT];
+  bool xrow_ok[XPT];
+  const uint16_t* xsrc[XPT];
+#pragma unroll
+  for (int m = 0; m < XPT; ++m) {
+    const int u = tid + 256 * m;
+    xr[m] = u / NP;
+    xp[m] = u % NP;
+    xrow_ok[m] = t0 + xr[m] < T;
+    xsrc[m] = x + (size_t)(xrow_ok[m] ? t0 + xr[m] : T - 1) * H;
+  }
+  const uint16_t* wrow[EPW];
+#pragma unroll
+  for (int et = 0; et < EPW; ++et) {
+    const int e = (wv * EPW + et) * 16 + c16;
+    wrow[et] = w + (size_t)(e < E ? e : E - 1) * H;
+  }
+
+  u32x4 xreg[D][XPT];
+  u32x4 wreg[D][EPW][PQ];
+  auto load_x = [&](int i, u32x4 (&dst)[XPT]) {
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+      const int kk = k_lo + i * KS + xp[m] * 8;
+      dst[m] = ld16_stream(xsrc[m] + (kk < H ? kk : H - 8));
+    }
+  };
+  auto load_w = [&](int i, u32x4 (&dst)[EPW][PQ]) {
+#pragma unroll
+    for (int et = 0; et < EPW; ++et)
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+        const int kk = k_lo + i * KS + g * (8 * PQ) + q * 8;
+        dst[et][q] = ld16(wrow[et] + (kk < H ? kk : H - 8));
+      }
+  };
+
+  f32x4 acc[TT][EPW];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_x(j, xreg[j]);
+    load_w(j, wreg[j]);
+  }
+  for (int i0 = 0; i0 < nss; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      unsigned char* slot = lds + (i & 1) * XSLOT;
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const bool ok = xrow_ok[m] && k_lo + i * KS + xp[m] * 8 < k_hi;
+        st16(slot + xr[m] * RB + ((xp[m] ^ (xr[m] & (NP - 1))) * 16),
+             ok ? xreg[j][m] : z);
+      }
+      lds_barrier();
+      load_x(i + D, xreg[j]);
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const int r = tt * 16 + c16;
+          const int p = g * PQ + q;
+          Frag<uint16_t> a;
+          a.v = *reinterpret_cast<const u32x4*>(slot + r * RB + ((p ^ (r & (NP - 1))) * 16));
+#pragma unroll
+          for (int et = 0; et < EPW; ++et) {
+            Frag<uint16_t> b;
+            b.v = wreg[j][et][q];
+            acc[tt][et] = mfma_step(a, b, acc[tt][et]);
+          }
+        }
+      }
+      load_w(i + D, wreg[j]);
+    }
+  }
+  float* out = partial + (size_t)ks * T * EP;
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) {
+      const int e = (wv * EPW + et) * 16 + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + tt * 16 + g * 4 + i;
+        if (t < T) out[(size_t)t * EP + e] = acc[tt][et][i];
+      }
+    }
+}
+
+// Sum of the S partial logits (ranges in ascending order) + bias, then the
+// top-k of every token.  A workgroup of WAVES waves covers
+// 4 * WAVES * PASSES tokens (4 per wave and pass); when that is one 64-token
+// tile it also writes the tile's histogram and slot ranks.
+template <int ET, int WAVES, int PASSES>
+__global__ __launch_bounds__(64 * WAVES) void gate_reduce_topk_kernel(
+    const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
+    const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ logits_dbg,
+    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int TOK = 4 * WAVES * PASSES;
+  constexpr bool HIST = TOK == 64;
+  __shared__ unsigned long long tile_bits[HIST ? 16 * ET : 1];
+  __shared__ int tile_sel[HIST ? 64 * MOE_MAX_TOPK : 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * TOK;
+  if constexpr (HIST) {
+    for (int e = tid; e < 16 * ET; e += NT) tile_bits[e] = 0ull;
+    __syncthreads();
+  }
+  float bv[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et) {
+    const int e = et * 16 + c16;
+    bv[et] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+  }
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int tl = (wv * PASSES + pass) * 4 + g;
+    const int t = t0 + tl;
+    const int tc = t < T ? t : T - 1;
+    // partial sums in ascending range order; loads batched four ranges at
+    // a time (clamped, unconditional) so they are in flight together
+    float v[ET];
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      const int e = et * 16 + c16;
+      v[et] = partial[(size_t)tc * EPS + (e < E ? e : 0)];
+    }
+    for (int q0 = 1; q0 < S; q0 += 4) {
+      float u[4][ET];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int q = q0 + b < S ? q0 + b : S - 1;
+        const float* pq = partial + ((size_t)q * T + tc) * EPS;
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          const int e = et * 16 + c16;
+          u[b][et] = pq[e < E ? e : 0];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (q0 + b < S) {
+#pragma unroll
+          for (int et = 0; et < ET; ++et) v[et] += u[b][et];
+        }
+    }
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      v[et] += bv[et];
+      const int e = et * 16 + c16;
+      if (logits_dbg != nullptr && t < T && e < E)
+        logits_dbg[(size_t)t * E + e] = v[et];
+    }
+    if constexpr (HIST)
+      topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w, tile_bits,
+                            tile_sel, tl);
+    else
+      topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w);
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    for (int e = tid; e < E; e += NT)
+      tile_base[(size_t)blockIdx.x * E + e] = __popcll(tile_bits[e]);
+    const int n = min(64, T - t0) * k;
+    for (int q = tid; q < n; q += NT) {
+      const int tl = q / k, j = q - tl * k;
+      const int e = tile_sel[tl * MOE_MAX_TOPK + j];
+      slot_rank[(size_t)t0 * k + q] =
+          __popcll(tile_bits[e] & ((1ull << tl) - 1ull));
+    }
+  }
+}
+
 // ------------------------------------------------------------------ gate, E < 64
 
 // One workgroup = 16 tokens; the 4 waves split the hidden dimension into
@@ -562,14 +780,17 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
   const int lo = active ? (int)((long long)p * ntiles / parts) : 0;
   const int hi = active ? (int)((long long)(p + 1) * ntiles / parts) : 0;
 
+  // loads are unconditional (clamped row) so a batch is in flight together
   int v[B];
   int sum = 0;
+  const int last = hi > lo ? hi - 1 : 0;
   for (int b0 = lo; b0 < hi; b0 += B) {
 #pragma unroll
     for (int u = 0; u < B; ++u)
-      v[u] = (b0 + u < hi) ? tile_base[(size_t)(b0 + u) * E + e] : 0;
+      v[u] = tile_base[(size_t)min(b0 + u, last) * E + e];
 #pragma unroll
-    for (int u = 0; u < B; ++u) sum += v[u];
+    for (int u = 0; u < B; ++u)
+      if (b0 + u < hi) sum += v[u];
   }
   if (active) part[p * E + e] = sum;
   __syncthreads();
@@ -609,7 +830,7 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
       if (!kept) {
 #pragma unroll
         for (int u = 0; u < B; ++u)
-          v[u] = (b0 + u < hi) ? tile_base[(size_t)(b0 + u) * E + e] : 0;
+          v[u] = tile_base[(size_t)min(b0 + u, last) * E + e];
       }
 #pragma unroll
       for (int u = 0; u < B; ++u) {
@@ -644,13 +865,77 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   }
   const dim3 grid((T + 63) / 64);
   if constexpr (sizeof(XT) == 2) {
+    const int epw = gate_epw(E);
+    // Split the hidden dimension so the partial GEMM runs about 256
+    // workgroups (128 for few tokens, whose reduction is the bottleneck).
+    // With 128-token tiles every gate-weight fragment a wave loads feeds 8
+    // MFMAs, which halves each CU's gate-weight traffic per token; that and
+    // a full chip beat the fused single pass even at 16K tokens.
+    const int TT = (epw <= 4 && T >= 8192) ? 8 : T >= 2048 ? 4 : 2;
+    const int tiles = (T + 16 * TT - 1) / (16 * TT);
+    const int target = T >= 2048 ? 256 : 128;
+    int S = (target + tiles - 1) / tiles;
+    S = min(S, min(split_max(T), (H + 63) / 64));
+    if (S > 1) {
+      const int KR = ((H + S - 1) / S + 63) / 64 * 64;
+      S = (H + KR - 1) / KR;
+      float* part = (float*)((unsigned char*)sr + ws_rank_bytes(T, k));
+      const dim3 pgrid(tiles, S);
+#define MOE_GATE_PART(EPWV, TTV, DV)                                           \
+  hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV>), pgrid,          \
+                     dim3(256), 0, s, x, w, T, H, E, KR, part)
+#define MOE_GATE_PART_E(TTV)                                                   \
+  do {                                                                         \
+    if (epw == 1) MOE_GATE_PART(1, TTV, 4);                                    \
+    else if (epw == 2) MOE_GATE_PART(2, TTV, 4);                               \
+    else if (epw == 4) MOE_GATE_PART(4, TTV, 4);                               \
+    else if (epw == 6) MOE_GATE_PART(6, TTV, 3);                               \
+    else MOE_GATE_PART(8, TTV, 2);                                             \
+  } while (0)
+      if (TT == 8) {
+        if (epw == 1) MOE_GATE_PART(1, 8, 3);
+        else if (epw == 2) MOE_GATE_PART(2, 8, 3);
+        else MOE_GATE_PART(4, 8, 2);
+      } else if (TT == 4) {
+        MOE_GATE_PART_E(4);
+      } else {
+        MOE_GATE_PART_E(2);
+      }
+#undef MOE_GATE_PART_E
+#undef MOE_GATE_PART
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      const int EPS = 64 * epw;
+      // reduction: 64-token workgroups (fused histogram) for many tokens,
+      // 16-token workgroups for few
+      const bool fuse = T >= 1024;
+      const dim3 rgrid(fuse ? (T + 63) / 64 : (T + 15) / 16);
+#define MOE_GATE_RED(ETV, WV, PS)                                              \
+  hipLaunchKernelGGL((gate_reduce_topk_kernel<ETV, WV, PS>), rgrid,           \
+                     dim3(64 * WV), 0, s, part, S, EPS, T, E, k, bias, idx,   \
+                     tw, dbg, tb, sr)
+#define MOE_GATE_RED_E(ETV, WV64, PS64)                                        \
+  do {                                                                         \
+    if (fuse) MOE_GATE_RED(ETV, WV64, PS64);                                   \
+    else MOE_GATE_RED(ETV, 4, 1);                                              \
+  } while (0)
+      if (epw == 1) MOE_GATE_RED_E(4, 16, 1);
+      else if (epw == 2) MOE_GATE_RED_E(8, 16, 1);
+      else if (epw == 4) MOE_GATE_RED_E(16, 8, 2);
+      else if (epw == 6) MOE_GATE_RED_E(24, 8, 2);
+      else MOE_GATE_RED_E(32, 4, 4);
+#undef MOE_GATE_RED_E
+#undef MOE_GATE_RED
+      *fused_hist = fuse;
+      return hipGetLastError();
+    }
 #define MOE_GATE_V2(EPWV, PQV, DV)                                         \
   hipLaunchKernelGGL((gate_topk_v2_kernel<EPWV, PQV, DV>), grid, dim3(256), \
                      0, s, x, w, bias, T, H, E, k, idx, tw, dbg, tb, sr)
-    if (et <= 4) MOE_GATE_V2(1, 2, 4);
-    else if (et <= 8) MOE_GATE_V2(2, 2, 4);
-    else if (et <= 16) MOE_GATE_V2(4, 2, 4);
-    else if (et <= 24) MOE_GATE_V2(6, 2, 3);
+    if (epw == 1) MOE_GATE_V2(1, 2, 4);
+    else if (epw == 2) MOE_GATE_V2(2, 2, 4);
+    else if (epw == 4) MOE_GATE_V2(4, 2, 4);
+    else if (epw == 6) MOE_GATE_V2(6, 2, 3);
     else MOE_GATE_V2(8, 2, 2);
 #undef MOE_GATE_V2
     *fused_hist = true;

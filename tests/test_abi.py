@@ -80,7 +80,7 @@ A = [0x10000000 * (i + 1) for i in range(16)]
 def _route(L, **kw):
     a = dict(x=A[0], xdt=1, T=100, H=256, w=A[1], E=16, bias=None, k=2, pad=4,
              idx=A[2], tw=A[3], counts=A[4], offsets=A[5], dbg=None, ws=A[6],
-             wsb=1 << 20, stream=None)
+             wsb=1 << 26, stream=None)
     a.update(kw)
     return L.moe_route(a["x"], a["xdt"], a["T"], a["H"], a["w"], a["E"],
                        a["bias"], a["k"], a["pad"], a["idx"], a["tw"],
@@ -98,7 +98,7 @@ def _route(L, **kw):
     (dict(x=A[0] + 8), ALIGN), (dict(w=A[1] + 4), ALIGN),
     (dict(wsb=100), WS),
     (dict(tw=A[0]), ALIAS), (dict(idx=A[1] + 64), ALIAS),
-    (dict(dbg=A[4]), ALIAS), (dict(ws=A[5]), ALIAS),
+    (dict(dbg=A[4]), ALIAS), (dict(ws=A[5] - 256), ALIAS),
 ])
 def test_route_validation(L, no_gpu, kw, want):
     assert _route(L, **kw) == want
@@ -106,7 +106,7 @@ def test_route_validation(L, no_gpu, kw, want):
 
 def _dispatch(L, **kw):
     a = dict(x=A[0], xdt=1, T=100, H=256, idx=A[1], k=2, E=16, pad=4,
-             counts=A[2], offsets=A[3], ws=A[4], wsb=1 << 20, pdt=1,
+             counts=A[2], offsets=A[3], ws=A[4], wsb=1 << 26, pdt=1,
              rows=A[5], cap=O.rows_capacity(100, 16, 2, 4), scales=None,
              row_src=A[6], tok_row=A[7], stream=None)
     a.update(kw)
@@ -159,7 +159,7 @@ def test_combine_validation(L, no_gpu, kw, want):
 
 def test_plan_validation(L, no_gpu):
     cap_ok = dict(idx=A[0], T=10, k=2, E=8, pad=1, counts=A[1], offsets=A[2],
-                  ws=A[3], wsb=1 << 16)
+                  ws=A[3], wsb=1 << 26)
 
     def call(**kw):
         a = dict(cap_ok)

@@ -41,6 +41,9 @@ SMALL = {
     "e40_k5": C["dsv3_decode"].with_shape(T=191, H=384, E=40, k=5, pad=16),
     "bf16_e100_h320": C["mixtral"].with_shape(T=130, H=320, E=100, k=4, pad=7),
     "bf16_e64_h200": C["mixtral"].with_shape(T=77, H=200, E=64, k=3, pad=2),
+    "split_t1500": C["dsv3_decode"].with_shape(T=1500, H=1024),
+    "split_t3000_e128": C["dsv3_prefill"].with_shape(T=3000, H=512, E=128,
+                                                     k=6, pad=32),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 
