@@ -11,7 +11,8 @@
 //   residual           = residual + MoE output
 // so the auxiliary stream never depends on the routed combine.
 //
-// Design for CDNA4: one wavefront per token.  Lanes 0..k-1 fetch the k
+// Design for CDNA4: one wavefront per token (several per token when there
+// are too few tokens to fill the chip).  Lanes 0..k-1 fetch the k
 // (row, weight) pairs, broadcast to scalar registers; each lane then owns
 // two groups of 8 consecutive hidden elements per step and issues all their
 // 16-byte row gathers plus the residual and shared loads before any
@@ -56,7 +57,9 @@ __device__ __forceinline__ void unpack8(const Chunk8<YT>& v, float f[8]) {
   }
 }
 
-// OUT: 0 = dual residual (bf16), 1 = routed-only bf16, 2 = routed-only fp32.
+// OUT: 0 = dual residual (bf16), 1 = routed-only bf16, 2 = routed-only fp32,
+// 3 = main residual stream only (bf16; the auxiliary stream comes from
+// farskip_aux_kernel).
 // Each lane keeps U = 2 groups of 8 elements in flight: for k = 8 that is
 // 2 * (8 gathers + shared + residual) 16-byte loads issued before any math.
 template <int KMAX, int YT, int OUT>
@@ -65,10 +68,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int32_t* __restrict__ tok_row, const float* __restrict__ topk_w,
     int T, int k, const unsigned char* __restrict__ shared,
     const unsigned char* res_in, unsigned char* res_out,
-    unsigned char* __restrict__ rnr, unsigned char* __restrict__ out) {
+    unsigned char* __restrict__ rnr, unsigned char* __restrict__ out,
+    int hsplit) {
   constexpr int U = 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wv;
+  // wave -> (token, part): with few tokens, hsplit waves share one token's
+  // hidden dimension (interleaved groups of 64*U chunks)
+  const int gw = blockIdx.x * 4 + wv;
+  const int t = gw / hsplit, part = gw - t * hsplit;
   if (t >= T) return;
 
   int r = -1;
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   if (lane < k) {
     const size_t s = (size_t)t * k + lane;
     r = tok_row[s];
-    wt = topk_w[s];
+    wt = topk_w != nullptr ? topk_w[s] : 1.0f;   // unit weights: plain sum
     if (r < 0 || (long long)r >= y_rows) r = -1;
   }
   int rj[KMAX];
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const size_t trow = (size_t)t * H * 2;     // byte offset of token row, bf16
   const int nc8 = H / 8;
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int c0 = lane; c0 < nc8; c0 += 64 * U) {
+  for (int c0 = part * 64 * U + lane; c0 < nc8; c0 += hsplit * 64 * U) {
     Chunk8<YT> g[U][KMAX];
     u32x4 shv[U], rsv[U];
 #pragma unroll
@@ -103,7 +110,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
         for (int j = 0; j < KMAX; ++j)
           if (rj[j] >= 0) g[u][j] = load8<YT>(y + (size_t)rj[j] * yrowb, c);
         shv[u] = shared != nullptr ? ld16_stream(shared + trow + (size_t)c * 16) : z;
-        if constexpr (OUT == 0) rsv[u] = ld16(res_in + trow + (size_t)c * 16);
+        if constexpr (OUT == 0 || OUT == 3)
+          rsv[u] = ld16(res_in + trow + (size_t)c * 16);
       }
     }
 #pragma unroll
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
         }
       }
       unpack8_bf16(shv[u], sh);
-      if constexpr (OUT == 0) {
+      if constexpr (OUT == 0 || OUT == 3) {
         float rs[8], o[8], a[8];
         unpack8_bf16(rsv[u], rs);
 #pragma unroll
@@ -132,7 +140,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
           a[i] = rs[i] + sh[i];
         }
         st16_stream(res_out + trow + (size_t)c * 16, pack8_bf16(o));
-        st16_stream(rnr + trow + (size_t)c * 16, pack8_bf16(a));
+        if constexpr (OUT == 0)
+          st16_stream(rnr + trow + (size_t)c * 16, pack8_bf16(a));
       } else {
         float o[8];
 #pragma unroll
@@ -161,16 +170,27 @@ static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                              const int32_t* tok_row, const float* w, int T,
                              int k, const unsigned char* sh,
                              const unsigned char* ri, unsigned char* ro,
-                             unsigned char* rn, unsigned char* out) {
+                             unsigned char* rn, unsigned char* out, int hs) {
   if (om == 0)
     hipLaunchKernelGGL((combine_kernel<KMAX, YT, 0>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out);
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
+  else if (om == 3)
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 3>), grid, dim3(256), 0, s, y,
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else if (om == 1)
     hipLaunchKernelGGL((combine_kernel<KMAX, YT, 1>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out);
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else
     hipLaunchKernelGGL((combine_kernel<KMAX, YT, 2>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out);
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
+}
+
+// Waves per token: enough waves in flight for few tokens (about 2048),
+// never more than the token row has 64*U-chunk groups.
+static int waves_per_token(int T, int groups_per_row) {
+  const int want = (2048 + T - 1) / T;
+  const int hs = want < groups_per_row ? want : groups_per_row;
+  return hs < 1 ? 1 : hs;
 }
 
 hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
@@ -178,8 +198,10 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
                           int k, const void* shared, const void* res_in,
                           void* res_out, void* rnr, void* out, int odt,
                           hipStream_t s) {
-  const dim3 grid((T + 3) / 4);
-  const int om = res_in != nullptr ? 0 : (odt == DT_BF16 ? 1 : 2);
+  const int hs = waves_per_token(T, (H / 8 + 127) / 128);
+  const dim3 grid((unsigned)(((long long)T * hs + 3) / 4));
+  const int om = res_in != nullptr ? (rnr != nullptr ? 0 : 3)
+                                   : (odt == DT_BF16 ? 1 : 2);
   const unsigned char* yb = (const unsigned char*)y;
   const unsigned char* sh = (const unsigned char*)shared;
   const unsigned char* ri = (const unsigned char*)res_in;
@@ -191,10 +213,10 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
   do {                                                                        \
     if (ydt == DT_BF16)                                                       \
       launch_combine_k<KV, 1>(om, grid, s, yb, yr, H, tok_row, topk_w, T, k,  \
-                              sh, ri, ro, rn, ob);                            \
+                              sh, ri, ro, rn, ob, hs);                        \
     else                                                                      \
       launch_combine_k<KV, 0>(om, grid, s, yb, yr, H, tok_row, topk_w, T, k,  \
-                              sh, ri, ro, rn, ob);                            \
+                              sh, ri, ro, rn, ob, hs);                        \
   } while (0)
   if (k <= 1) MOE_COMB(1);
   else if (k <= 2) MOE_COMB(2);
@@ -202,6 +224,144 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
   else if (k <= 8) MOE_COMB(8);
   else MOE_COMB(16);
 #undef MOE_COMB
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ FarSkip auxiliary stream
+
+// residual_no_routed = bf16(residual + shared): the auxiliary stream of the
+// dual residual update, which needs neither the router nor the routed
+// combine and can therefore be produced before them (the next layer's
+// attention reads this stream while the routed combine is still pending).
+__global__ __launch_bounds__(256) void farskip_aux_kernel(
+    const unsigned char* __restrict__ shared,
+    const unsigned char* __restrict__ residual,
+    unsigned char* __restrict__ rnr, long long n16) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (long long)gridDim.x * 256) {
+    float sh[8], rs[8], a[8];
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    unpack8_bf16(shared != nullptr ? ld16_stream(shared + i * 16) : z, sh);
+    unpack8_bf16(ld16_stream(residual + i * 16), rs);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = rs[q] + sh[q];
+    st16_stream(rnr + i * 16, pack8_bf16(a));
+  }
+}
+
+hipError_t launch_farskip_aux(const void* shared, const void* residual,
+                              void* rnr, int T, int H, hipStream_t s) {
+  const long long n16 = (long long)T * H / 8;
+  long long blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(farskip_aux_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     s, (const unsigned char*)shared,
+                     (const unsigned char*)residual, (unsigned char*)rnr, n16);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ backward
+
+// Backward of the weighted combine routed[t] = sum_j w[t,j] * y[tok_row[t,j]]
+// for an upstream gradient g = dL/d routed:
+//   grad_y[tok_row[t,j]] = w[t,j] * g[t]            (bf16, one write per row)
+//   grad_w[t,j]          = sum_h g[t,h] * y[tok_row[t,j],h]   (fp32)
+// One wave per token; each lane keeps k partial dot products over its
+// hidden elements, reduced across the wave in a fixed order at the end.
+template <int KMAX, int YT>
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const unsigned char* __restrict__ g, const unsigned char* __restrict__ y,
+    long long y_rows, int H, const int32_t* __restrict__ tok_row,
+    const float* __restrict__ topk_w, int T, int k,
+    unsigned char* __restrict__ grad_y, float* __restrict__ grad_w) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  int r = -1;
+  float wt = 0.0f;
+  if (lane < k) {
+    const size_t s = (size_t)t * k + lane;
+    r = tok_row[s];
+    wt = topk_w[s];
+    if (r < 0 || (long long)r >= y_rows) r = -1;
+  }
+  int rj[KMAX];
+  float wj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    rj[j] = (j < k) ? __builtin_amdgcn_readlane(r, j) : -1;
+    wj[j] = (j < k) ? __uint_as_float(__builtin_amdgcn_readlane(
+                          __float_as_uint(wt), j))
+                    : 0.0f;
+  }
+  const size_t yrowb = (size_t)H * (YT == 1 ? 2 : 4);
+  const size_t trow = (size_t)t * H * 2;
+  const int nc8 = H / 8;
+  float dot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) dot[j] = 0.0f;
+  for (int c = lane; c < nc8; c += 64) {
+    float gf[8];
+    unpack8_bf16(ld16_stream(g + trow + (size_t)c * 16), gf);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (rj[j] < 0) continue;
+      float yf[8], d[8];
+      if constexpr (YT == 1) {
+        unpack8_bf16(ld16(y + (size_t)rj[j] * yrowb + (size_t)c * 16), yf);
+      } else {
+        const u32x4 a = ld16(y + (size_t)rj[j] * yrowb + (size_t)c * 32);
+        const u32x4 b = ld16(y + (size_t)rj[j] * yrowb + (size_t)c * 32 + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          yf[i] = __uint_as_float(a[i]);
+          yf[4 + i] = __uint_as_float(b[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dot[j] = fmaf(gf[i], yf[i], dot[j]);
+        d[i] = wj[j] * gf[i];
+      }
+      st16_stream(grad_y + (size_t)rj[j] * H * 2 + (size_t)c * 16,
+                  pack8_bf16(d));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    float v = dot[j];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if (lane == 0 && j < k) grad_w[(size_t)t * k + j] = v;
+  }
+}
+
+hipError_t launch_combine_backward(const void* g, const void* y, int ydt,
+                                   int H, size_t y_rows,
+                                   const int32_t* tok_row,
+                                   const float* topk_w, int T, int k,
+                                   void* grad_y, float* grad_w,
+                                   hipStream_t s) {
+  const dim3 grid((T + 3) / 4);
+  const unsigned char* gb = (const unsigned char*)g;
+  const unsigned char* yb = (const unsigned char*)y;
+  unsigned char* dyb = (unsigned char*)grad_y;
+  const long long yr = (long long)y_rows;
+#define MOE_CBWD(KV)                                                           \
+  do {                                                                         \
+    if (ydt == DT_BF16)                                                        \
+      hipLaunchKernelGGL((combine_backward_kernel<KV, 1>), grid, dim3(256), 0, \
+                         s, gb, yb, yr, H, tok_row, topk_w, T, k, dyb, grad_w);\
+    else                                                                       \
+      hipLaunchKernelGGL((combine_backward_kernel<KV, 0>), grid, dim3(256), 0, \
+                         s, gb, yb, yr, H, tok_row, topk_w, T, k, dyb, grad_w);\
+  } while (0)
+  if (k <= 1) MOE_CBWD(1);
+  else if (k <= 2) MOE_CBWD(2);
+  else if (k <= 4) MOE_CBWD(4);
+  else if (k <= 8) MOE_CBWD(8);
+  else MOE_CBWD(16);
+#undef MOE_CBWD
   return hipGetLastError();
 }
 

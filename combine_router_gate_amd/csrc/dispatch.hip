@@ -12,7 +12,9 @@
 // + rank of t among the tile's tokens that chose e, i.e. ascending token
 // order inside every expert segment.
 //
-// Design for CDNA4: one wavefront per token.  Lanes 0..k-1 resolve the k
+// Design for CDNA4: one wavefront per token (several per token when there
+// are too few tokens to fill the chip, each taking an interleaved share of
+// the row).  Lanes 0..k-1 resolve the k
 // destination rows, which are then broadcast to scalar registers; the token
 // row is read from HBM once in 16-byte vectors (coalesced across the wave)
 // and written k times with streaming (non-temporal) stores, which measured
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
     const int32_t* __restrict__ slot_rank, unsigned char* __restrict__ rows,
     long long capacity, float* __restrict__ row_scales,
     int32_t* __restrict__ row_src, int32_t* __restrict__ tok_row,
-    int tok_blocks) {
+    int tok_blocks, int hsplit) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if ((int)blockIdx.x >= tok_blocks) {
     // padding rows of every expert, then every row past offsets[E]
@@ -79,12 +81,15 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
       row_src[r] = -1;
     return;
   }
-  const int t = blockIdx.x * 4 + wv;
+  // wave -> (token, part): with few tokens, hsplit waves share one token's
+  // row (interleaved groups of 64-lane chunks); part 0 writes the metadata
+  const int gw = blockIdx.x * 4 + wv;
+  const int t = gw / hsplit, part = gw - t * hsplit;
   if (t >= T) return;
 
   const int r =
       token_row(t, lane, k, E, capacity, topk_idx, tile_base, slot_rank);
-  if (lane < k) {
+  if (lane < k && part == 0) {
     tok_row[(size_t)t * k + lane] = r;
     if (r >= 0) row_src[r] = t;
   }
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
     const int nc = (int)(rowb / 16);
     const unsigned char* src = x + (size_t)t * rowb;
     constexpr int U = 2;
-    for (int c0 = 0; c0 < nc; c0 += 64 * U) {
+    for (int c0 = part * 64 * U; c0 < nc; c0 += hsplit * 64 * U) {
       u32x4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
     const int nc16 = H / 16;
     const int nblk = H / kFp8Block;
     const unsigned char* src = x + (size_t)t * H * esize;
-    for (int c0 = 0; c0 < nc16; c0 += 64) {
+    for (int c0 = part * 64; c0 < nc16; c0 += hsplit * 64) {
       const int c = c0 + lane;
       const bool ok = c < nc16;
       float f[16];
@@ -247,19 +252,20 @@ static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
                               const int32_t* counts, const int32_t* offsets,
                               const int32_t* tb, const int32_t* sr,
                               unsigned char* rows, long long cap, float* sc,
-                              int32_t* row_src, int32_t* tok_row, int tblocks) {
+                              int32_t* row_src, int32_t* tok_row, int tblocks,
+                              int hs) {
   if (mode == 0)
     hipLaunchKernelGGL((dispatch_kernel<KMAX, 0>), grid, dim3(256), 0, s, x,
                        esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
-                       cap, sc, row_src, tok_row, tblocks);
+                       cap, sc, row_src, tok_row, tblocks, hs);
   else if (mode == 1)
     hipLaunchKernelGGL((dispatch_kernel<KMAX, 1>), grid, dim3(256), 0, s, x,
                        esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
-                       cap, sc, row_src, tok_row, tblocks);
+                       cap, sc, row_src, tok_row, tblocks, hs);
   else
     hipLaunchKernelGGL((dispatch_kernel<KMAX, 2>), grid, dim3(256), 0, s, x,
                        esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
-                       cap, sc, row_src, tok_row, tblocks);
+                       cap, sc, row_src, tok_row, tblocks, hs);
 }
 
 hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
@@ -273,7 +279,13 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
       (const int32_t*)((const unsigned char*)workspace + ws_tile_bytes(T, E));
   const int esize = xdt == DT_F32 ? 4 : 2;
   const int mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
-  const int tblocks = (T + 3) / 4;
+  // waves per token: about 2048 waves in flight for few tokens, at most one
+  // per group of 64-lane chunks of the row
+  const int groups = mode == 0 ? (H * esize / 16 + 127) / 128 : (H / 16 + 63) / 64;
+  int hs = (2048 + T - 1) / (T > 0 ? T : 1);
+  hs = hs < groups ? hs : groups;
+  hs = hs < 1 ? 1 : hs;
+  const int tblocks = (int)(((long long)T * hs + 3) / 4);
   const dim3 grid(tblocks + kDispatchFillBlocks);
   const unsigned char* xb = (const unsigned char*)x;
   unsigned char* rb = (unsigned char*)rows;
@@ -281,7 +293,7 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
 #define MOE_DISPATCH_K(KV)                                                   \
   launch_dispatch_k<KV>(mode, grid, s, xb, esize, T, H, topk_idx, k, E,      \
                         counts, offsets, tb, sr, rb, cap, row_scales,        \
-                        row_src, tok_row, tblocks)
+                        row_src, tok_row, tblocks, hs)
   if (k <= 1) MOE_DISPATCH_K(1);
   else if (k <= 2) MOE_DISPATCH_K(2);
   else if (k <= 4) MOE_DISPATCH_K(4);

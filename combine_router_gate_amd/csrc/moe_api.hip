@@ -214,8 +214,7 @@ int moe_combine_residual(const void* y, int y_dtype, int H, size_t y_rows,
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   const bool dual = residual_in != nullptr;
   if (dual) {
-    if (residual_out == nullptr || residual_no_routed == nullptr)
-      return MOE_ERR_NULL;
+    if (residual_out == nullptr) return MOE_ERR_NULL;
     if (out != nullptr) return MOE_ERR_ALIAS;
   } else {
     if (out == nullptr) return MOE_ERR_NULL;
@@ -254,6 +253,75 @@ int moe_combine_residual(const void* y, int y_dtype, int H, size_t y_rows,
       y, y_dtype, H, y_rows, tok_row, topk_w, T, k, shared, residual_in,
       residual_out, residual_no_routed, out, dual ? MOE_BF16 : out_dtype,
       (hipStream_t)stream));
+}
+
+int moe_farskip_aux(const void* shared, const void* residual_in,
+                    void* residual_no_routed, int T, int H, void* stream) {
+  if (T < 0 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (residual_in == nullptr || residual_no_routed == nullptr)
+    return MOE_ERR_NULL;
+  if (!aligned(shared, 16) || !aligned(residual_in, 16) ||
+      !aligned(residual_no_routed, 16))
+    return MOE_ERR_ALIGN;
+  const size_t tb = (size_t)T * H * 2;
+  const Span ins[] = {{shared, shared ? tb : 0}, {residual_in, tb}};
+  const Span outs[] = {{residual_no_routed, tb}};
+  if (any_overlap(outs, 1, ins, 2)) return MOE_ERR_ALIAS;
+  return hip_status(moe::launch_farskip_aux(shared, residual_in,
+                                            residual_no_routed, T, H,
+                                            (hipStream_t)stream));
+}
+
+int moe_combine_backward(const void* grad_out, const void* y, int y_dtype,
+                         int H, size_t y_rows, const int32_t* tok_row,
+                         const float* topk_w, int T, int k, void* grad_y,
+                         float* grad_w, void* stream) {
+  if (T < 0 || H < 8 || H % 8 != 0 || k < 1 || k > MOE_MAX_TOPK)
+    return MOE_ERR_SHAPE;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (grad_out == nullptr || y == nullptr || tok_row == nullptr ||
+      topk_w == nullptr || grad_y == nullptr || grad_w == nullptr)
+    return MOE_ERR_NULL;
+  if (!aligned(grad_out, 16) || !aligned(y, 16) || !aligned(grad_y, 16) ||
+      !aligned(tok_row, 4) || !aligned(topk_w, 4) || !aligned(grad_w, 4))
+    return MOE_ERR_ALIGN;
+  const Span ins[] = {{grad_out, (size_t)T * H * 2},
+                      {y, y_rows * H * dtype_size(y_dtype)},
+                      {tok_row, (size_t)T * k * 4},
+                      {topk_w, (size_t)T * k * 4}};
+  const Span outs[] = {{grad_y, y_rows * H * 2}, {grad_w, (size_t)T * k * 4}};
+  if (any_overlap(outs, 2, ins, 4)) return MOE_ERR_ALIAS;
+  return hip_status(moe::launch_combine_backward(
+      grad_out, y, y_dtype, H, y_rows, tok_row, topk_w, T, k, grad_y, grad_w,
+      (hipStream_t)stream));
+}
+
+int moe_dispatch_backward(const void* grad_rows, int rows_dtype, int H,
+                          size_t rows_capacity, const int32_t* tok_row, int T,
+                          int k, void* grad_x, int grad_x_dtype,
+                          void* stream) {
+  if (T < 0 || H < 8 || H % 8 != 0 || k < 1 || k > MOE_MAX_TOPK)
+    return MOE_ERR_SHAPE;
+  if (rows_dtype != MOE_F32 && rows_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (grad_x_dtype != MOE_F32 && grad_x_dtype != MOE_BF16)
+    return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (grad_rows == nullptr || tok_row == nullptr || grad_x == nullptr)
+    return MOE_ERR_NULL;
+  if (!aligned(grad_rows, 16) || !aligned(grad_x, 16) || !aligned(tok_row, 4))
+    return MOE_ERR_ALIGN;
+  const Span ins[] = {{grad_rows, rows_capacity * H * dtype_size(rows_dtype)},
+                      {tok_row, (size_t)T * k * 4}};
+  const Span outs[] = {{grad_x, (size_t)T * H * dtype_size(grad_x_dtype)}};
+  if (any_overlap(outs, 1, ins, 2)) return MOE_ERR_ALIAS;
+  // an unweighted combine: grad_x[t] = sum_j grad_rows[tok_row[t, j]]
+  return hip_status(moe::launch_combine(grad_rows, rows_dtype, H,
+                                        rows_capacity, tok_row, nullptr, T, k,
+                                        nullptr, nullptr, nullptr, nullptr,
+                                        grad_x, grad_x_dtype,
+                                        (hipStream_t)stream));
 }
 
 int moe_expert_fixture(const void* rows, int payload_dtype,

@@ -76,6 +76,16 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
                           void* res_out, void* rnr, void* out, int odt,
                           hipStream_t s);
 
+hipError_t launch_farskip_aux(const void* shared, const void* residual,
+                              void* rnr, int T, int H, hipStream_t s);
+
+hipError_t launch_combine_backward(const void* g, const void* y, int ydt,
+                                   int H, size_t y_rows,
+                                   const int32_t* tok_row,
+                                   const float* topk_w, int T, int k,
+                                   void* grad_y, float* grad_w,
+                                   hipStream_t s);
+
 hipError_t launch_fixture(const void* rows, int pdt, const float* row_scales,
                           int H, const int32_t* row_src,
                           const int32_t* offsets, int E, const float* sigma,

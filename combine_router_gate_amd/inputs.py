@@ -26,6 +26,7 @@ from typing import Dict, Optional
 import numpy as np
 
 TID_X, TID_W, TID_PERM, TID_SIGMA, TID_SHARED, TID_RESID = 1, 2, 3, 4, 5, 6
+TID_GRAD = 7
 
 # Zipf exponent of the skewed workload and the strength with which its
 # log-probabilities enter the router logits.  0.17 gives a max/mean expert
@@ -188,3 +189,11 @@ def integer_workload(cfg: Config, seed: int = 0, lo: int = -2,
     base.w_gate = _pack(rw.astype(np.float32), cfg.x_dtype)
     return base
 
+
+
+def grad_tensor(seed: int, shape, dtype: str = "bf16", std: float = 1.0,
+                stream: int = 0) -> Tensor:
+    """Upstream gradient for the backward passes: N(0, std^2), rounded to
+    ``dtype``.  ``stream`` separates several gradients of one seed."""
+    return _pack(_normal(seed, TID_GRAD * 1000 + stream, tuple(shape), std),
+                 dtype)

@@ -43,6 +43,11 @@ _SIGS = {
                                   _vp, _vp, _vp, _vp, _i, _vp]),
     "moe_expert_fixture": (_i, [_vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz,
                                 _vp, _i, _vp]),
+    "moe_farskip_aux": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
+    "moe_combine_backward": (_i, [_vp, _vp, _i, _i, _sz, _vp, _vp, _i, _i,
+                                  _vp, _vp, _vp]),
+    "moe_dispatch_backward": (_i, [_vp, _i, _i, _sz, _vp, _i, _i, _vp, _i,
+                                   _vp]),
 }
 
 
@@ -182,6 +187,36 @@ def moe_expert_fixture(rows, payload_dtype, row_scales, row_src, offsets,
     _check(st, "moe_expert_fixture")
 
 
+def moe_farskip_aux(shared, residual_in, residual_no_routed, stream=None):
+    T, H = residual_in.shape
+    st = lib().moe_farskip_aux(_ptr(shared), _ptr(residual_in),
+                               _ptr(residual_no_routed), T, H,
+                               stream if stream is not None else
+                               _stream(residual_in.device))
+    _check(st, "moe_farskip_aux")
+
+
+def moe_combine_backward(grad_out, y, tok_row, topk_w, grad_y, grad_w,
+                         stream=None):
+    T, k = tok_row.shape
+    H = y.shape[1]
+    st = lib().moe_combine_backward(
+        _ptr(grad_out), _ptr(y), _dt(y), H, y.shape[0], _ptr(tok_row),
+        _ptr(topk_w), T, k, _ptr(grad_y), _ptr(grad_w),
+        stream if stream is not None else _stream(y.device))
+    _check(st, "moe_combine_backward")
+
+
+def moe_dispatch_backward(grad_rows, tok_row, grad_x, stream=None):
+    T, k = tok_row.shape
+    H = grad_rows.shape[1]
+    st = lib().moe_dispatch_backward(
+        _ptr(grad_rows), _dt(grad_rows), H, grad_rows.shape[0], _ptr(tok_row),
+        T, k, _ptr(grad_x), _dt(grad_x),
+        stream if stream is not None else _stream(grad_rows.device))
+    _check(st, "moe_dispatch_backward")
+
+
 # ----------------------------------------------------------------- allocating
 
 def route(x: torch.Tensor, w_gate: torch.Tensor, k: int, pad: int,
@@ -276,3 +311,40 @@ def combine_residual(y: torch.Tensor, tok_row: torch.Tensor,
     out = torch.empty((T, H), dtype=out_dtype, device=y.device)
     moe_combine_residual(y, tok_row, topk_w, shared, None, None, None, out)
     return out
+
+
+def farskip_aux(shared: Optional[torch.Tensor],
+                residual: torch.Tensor) -> torch.Tensor:
+    """Auxiliary stream residual + shared (bf16), before any routing."""
+    rnr = torch.empty_like(residual)
+    moe_farskip_aux(shared, residual, rnr)
+    return rnr
+
+
+def combine_main_residual(y, tok_row, topk_w, shared, residual,
+                          in_place: bool = False) -> torch.Tensor:
+    """Main stream residual + routed + shared only (split form)."""
+    res_out = residual if in_place else torch.empty_like(residual)
+    moe_combine_residual(y, tok_row, topk_w, shared, residual, res_out, None,
+                         None)
+    return res_out
+
+
+def combine_backward(grad_out, y, tok_row, topk_w):
+    """(grad_y, grad_w) of the weighted combine; grad_y rows that no slot
+    references are zero here (the kernel leaves them unwritten)."""
+    T, k = tok_row.shape
+    grad_y = torch.zeros((y.shape[0], y.shape[1]), dtype=torch.bfloat16,
+                         device=y.device)
+    grad_w = torch.empty((T, k), dtype=torch.float32, device=y.device)
+    moe_combine_backward(grad_out, y, tok_row, topk_w, grad_y, grad_w)
+    return grad_y, grad_w
+
+
+def dispatch_backward(grad_rows, tok_row, out_dtype=torch.float32):
+    """grad_x[t] = sum_j grad_rows[tok_row[t, j]]."""
+    T = tok_row.shape[0]
+    grad_x = torch.empty((T, grad_rows.shape[1]), dtype=out_dtype,
+                         device=grad_rows.device)
+    moe_dispatch_backward(grad_rows, tok_row, grad_x)
+    return grad_x

@@ -13,6 +13,9 @@
  *                        with one fp32 scale per 1x128 block)
  *   moe_combine_residual weighted gather-combine back to token order, fused
  *                        with the FarSkip-Collective dual residual update
+ *   moe_farskip_aux      the auxiliary residual stream alone (split form)
+ *   moe_combine_backward, moe_dispatch_backward
+ *                        gradients through the same routing plan
  *   moe_expert_fixture   a stand-in expert (y = sigma_e * row) for tests and
  *                        benchmarks; not part of the transform
  *
@@ -20,7 +23,9 @@
  *   - Device pointers.  Every array argument is device memory (HBM) that the
  *     caller allocated and owns; the library never allocates, frees or keeps
  *     a pointer after the call returns.  Arrays are dense row-major with the
- *     shapes given below and 16-byte aligned base addresses.
+ *     shapes given below.  Arrays read or written as 16-byte vectors (x,
+ *     w_gate, rows, y, shared, residuals, out, gradients of those, workspace)
+ *     need 16-byte aligned base addresses; the others their element size.
  *   - Asynchrony.  Each call validates its arguments on the host, then only
  *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
  *     and returns.  No call synchronises the device or copies device data to
@@ -91,7 +96,9 @@ int moe_last_hip_error(void);
 size_t moe_rows_capacity(int T, int E, int k, int pad);
 
 /* Bytes of scratch that moe_route / moe_plan write and moe_dispatch reads
- * (per-tile expert counts and prefixes, per-slot ranks).  0 if T == 0. */
+ * (per-tile expert counts and prefixes, per-slot ranks, and for fewer than
+ * 32768 tokens room for partial gate logits when the gate splits the hidden
+ * dimension).  0 if T == 0. */
 size_t moe_workspace_bytes(int T, int E, int k);
 
 /*
@@ -209,7 +216,9 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
  *   residual_in        [T, H] bf16
  *   residual_out       [T, H] bf16 = bf16(residual + routed + shared); may be
  *                      the same pointer as residual_in (in-place update)
- *   residual_no_routed [T, H] bf16 = bf16(residual + shared)
+ *   residual_no_routed [T, H] bf16 = bf16(residual + shared), or NULL when
+ *                      moe_farskip_aux produced it earlier (split form: the
+ *                      auxiliary stream does not wait for the routed combine)
  *   out must be NULL
  * routed-only form (residual_in == NULL):
  *   out [T, H] out_dtype (MOE_BF16 or MOE_F32) = routed + shared
@@ -224,6 +233,48 @@ int moe_combine_residual(const void* y, int y_dtype, int H, size_t y_rows,
                          void* residual_no_routed,
                          void* out, int out_dtype,
                          void* stream);
+
+/*
+ * moe_farskip_aux -- the auxiliary residual stream alone:
+ *   residual_no_routed[T, H] = bf16(residual_in + shared)   (shared NULL = 0)
+ * The FarSkip-Collective dual residual streams (Instella-MoE article, the
+ * dual residual streams and the four-line update) let the next layer's
+ * attention read this stream while the routed combine is still pending, so
+ * it can be produced before routing; the main stream then comes from
+ * moe_combine_residual with residual_no_routed = NULL.  Bit-identical to the
+ * fused form.  All arrays bf16 [T, H]; the output may not overlap the inputs.
+ */
+int moe_farskip_aux(const void* shared, const void* residual_in,
+                    void* residual_no_routed, int T, int H, void* stream);
+
+/*
+ * moe_combine_backward -- gradient of the weighted combine through the
+ * routing plan of the forward pass (MoonEP's backward reuses the forward
+ * plan: "MoonEP developer guide", core API example, backward).
+ * With routed[t] = sum_j topk_w[t,j] * y[tok_row[t,j]] and an upstream
+ * gradient grad_out = dL/d routed ([T, H] bf16; for the dual residual form
+ * this is the gradient of residual_out):
+ *   grad_y[tok_row[t,j]] = bf16(topk_w[t,j] * grad_out[t])   [y_rows, H] bf16
+ *   grad_w[t,j] = sum_h grad_out[t,h] * y[tok_row[t,j],h]   [T, k] fp32
+ * Rows of grad_y that no slot references are not written.  y_dtype is
+ * MOE_BF16 or MOE_F32.  Sums are fp32 in a fixed order (deterministic).
+ */
+int moe_combine_backward(const void* grad_out, const void* y, int y_dtype,
+                         int H, size_t y_rows, const int32_t* tok_row,
+                         const float* topk_w, int T, int k, void* grad_y,
+                         float* grad_w, void* stream);
+
+/*
+ * moe_dispatch_backward -- gradient of the scatter: every row is a copy of
+ * its token, so grad_x[t] = sum_j grad_rows[tok_row[t,j]] (an unweighted
+ * combine; slots whose row lies outside [0, rows_capacity) add nothing).
+ *   grad_rows [rows_capacity, H] rows_dtype (MOE_BF16 or MOE_F32)
+ *   grad_x    [T, H] grad_x_dtype (MOE_BF16 or MOE_F32), fp32 accumulation
+ */
+int moe_dispatch_backward(const void* grad_rows, int rows_dtype, int H,
+                          size_t rows_capacity, const int32_t* tok_row, int T,
+                          int k, void* grad_x, int grad_x_dtype,
+                          void* stream);
 
 /*
  * moe_expert_fixture -- stand-in expert used by tests and benchmarks in

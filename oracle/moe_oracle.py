@@ -327,6 +327,44 @@ def farskip_update(routed64, shared, residual):
             bf16_bits(round_to_bf16(rnr)), res_exact)
 
 
+def combine_backward(grad_out, y_values, tok_row, topk_w, y_rows: int):
+    """Gradient of the weighted combine routed[t] = sum_j w[t, j] *
+    y[tok_row[t, j]] for an upstream gradient grad_out = dL/d routed.  The
+    backward pass runs through the forward routing plan ("MoonEP developer
+    guide", core API example, backward); the gradients themselves are the
+    chain rule of a bilinear map:
+      dL/dy[tok_row[t, j]] = w[t, j] * grad_out[t]
+      dL/dw[t, j]          = <grad_out[t], y[tok_row[t, j]]>
+    Float64.  Returns (grad_y [y_rows, H], grad_w [T, k]); rows of grad_y that
+    no slot references are zero."""
+    g = np.asarray(grad_out, dtype=np.float64)
+    y = np.asarray(y_values, dtype=np.float64)
+    tr = np.asarray(tok_row, dtype=np.int64)
+    T, k = tr.shape
+    grad_y = np.zeros((y_rows, g.shape[1]), dtype=np.float64)
+    grad_w = np.zeros((T, k), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            r = tr[t, j]
+            grad_y[r] = np.float64(topk_w[t, j]) * g[t]
+            grad_w[t, j] = np.dot(g[t], y[r])
+    return grad_y, grad_w
+
+
+def dispatch_backward(grad_rows, tok_row) -> np.ndarray:
+    """Gradient of the scatter: every row of the expert-major buffer holds a
+    copy of its token, so dL/dx[t] = sum_j dL/drows[tok_row[t, j]] (float64;
+    the transpose of the row copy of the dispatch step)."""
+    gr = np.asarray(grad_rows, dtype=np.float64)
+    tr = np.asarray(tok_row, dtype=np.int64)
+    T, k = tr.shape
+    out = np.zeros((T, gr.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            out[t] += gr[tr[t, j]]
+    return out
+
+
 def routed_output(routed64, out_dtype: str):
     """Routed-only output (no residual): float32 values or bf16 bits."""
     if out_dtype == "f32":

@@ -143,7 +143,8 @@ def _combine(L, **kw):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(y=None), NULL), (dict(rnr=None), NULL), (dict(res_out=None), NULL),
+    (dict(y=None), NULL), (dict(res_out=None), NULL),
+    (dict(rnr=None, res_out=A[4] + 64), ALIAS),             # split form, partial overlap
     (dict(out=A[7]), ALIAS),                                  # out with residual
     (dict(res_in=None, res_out=None, rnr=None), NULL),        # no out at all
     (dict(res_in=None, out=A[7]), ALIAS),                     # stray residual_out
@@ -172,3 +173,58 @@ def test_plan_validation(L, no_gpu):
     assert call(wsb=1) == WS
     assert call(counts=A[0]) == ALIAS
     assert call(counts=A[1] + 2) == ALIGN
+
+
+def test_farskip_aux_validation(L, no_gpu):
+    def call(**kw):
+        a = dict(shared=A[0], res_in=A[1], rnr=A[2], T=100, H=256)
+        a.update(kw)
+        return L.moe_farskip_aux(a["shared"], a["res_in"], a["rnr"], a["T"],
+                                 a["H"], None)
+    assert call(T=-1) == SHAPE
+    assert call(H=12) == SHAPE
+    assert call(res_in=None) == NULL
+    assert call(rnr=None) == NULL
+    assert call(rnr=A[2] + 8) == ALIGN
+    assert call(rnr=A[1] + 256) == ALIAS
+    assert call(rnr=A[0]) == ALIAS
+    assert call(T=0, res_in=None, rnr=None) == OK       # empty: nothing to do
+
+
+def test_combine_backward_validation(L, no_gpu):
+    def call(**kw):
+        a = dict(g=A[0], y=A[1], ydt=1, H=256, y_rows=1000, tok_row=A[2],
+                 tw=A[3], T=100, k=2, gy=A[4], gw=A[5])
+        a.update(kw)
+        return L.moe_combine_backward(a["g"], a["y"], a["ydt"], a["H"],
+                                      a["y_rows"], a["tok_row"], a["tw"],
+                                      a["T"], a["k"], a["gy"], a["gw"], None)
+    assert call(k=0) == SHAPE
+    assert call(H=100) == SHAPE
+    assert call(ydt=2) == DTYPE
+    for name in ["g", "y", "tok_row", "tw", "gy", "gw"]:
+        assert call(**{name: None}) == NULL, name
+    assert call(gy=A[4] + 4) == ALIGN
+    assert call(gw=A[5] + 2) == ALIGN
+    assert call(gy=A[1]) == ALIAS
+    assert call(gw=A[3]) == ALIAS
+    assert call(gy=A[0] + 512) == ALIAS
+
+
+def test_dispatch_backward_validation(L, no_gpu):
+    def call(**kw):
+        a = dict(gr=A[0], rdt=1, H=256, cap=1000, tok_row=A[1], T=100, k=2,
+                 gx=A[2], xdt=0)
+        a.update(kw)
+        return L.moe_dispatch_backward(a["gr"], a["rdt"], a["H"], a["cap"],
+                                       a["tok_row"], a["T"], a["k"], a["gx"],
+                                       a["xdt"], None)
+    assert call(k=17) == SHAPE
+    assert call(H=4) == SHAPE
+    assert call(rdt=2) == DTYPE
+    assert call(xdt=2) == DTYPE
+    assert call(gr=None) == NULL
+    assert call(gx=None) == NULL
+    assert call(gx=A[2] + 8) == ALIGN
+    assert call(gx=A[0] + 256) == ALIAS
+    assert call(gx=A[1]) == ALIAS

@@ -413,6 +413,87 @@ def test_farskip_shared_zero_and_difference():
     assert np.abs(diff - routed).max() < 0.07     # two bf16 roundings
 
 
+# ------------------------------------------------------------------ backward
+
+def test_combine_backward_golden():
+    d = {}
+    for ln in _golden_lines("combine_backward_worked.txt"):
+        key, *vals = ln.split()
+        d[key] = np.array([float(v) for v in vals])
+    y = d["y"].reshape(3, 2)
+    tok_row = d["tok_row"].astype(np.int64).reshape(1, 2)
+    w = d["w"].reshape(1, 2)
+    g = d["g"].reshape(1, 2)
+    gy, gw = O.combine_backward(g, y, tok_row, w, 3)
+    assert np.array_equal(gw, d["grad_w"].reshape(1, 2))
+    assert np.array_equal(gy, d["grad_y"].reshape(3, 2))
+    assert np.array_equal(O.dispatch_backward(gy, tok_row),
+                          d["grad_x"].reshape(1, 2))
+
+
+def _backward_case(seed=4):
+    cfg = I.CONFIGS["mixtral"].with_shape(T=37, H=64, E=6, k=2, pad=4)
+    wl, r, tok_row, row_src, rows, _, y, routed = _chain(cfg, seed)
+    g = np.random.default_rng(seed).standard_normal((cfg.T, cfg.H))
+    return cfg, r, tok_row, row_src, y, g
+
+
+def test_combine_backward_adjoint_identity():
+    """L = <g, combine(y, w)> is linear in y and in w separately, so
+    L = <dL/dy, y> = <dL/dw, w> (Euler's identity for degree-1 maps), with
+    the forward taken from the pinned O.combine."""
+    cfg, r, tok_row, row_src, y, g = _backward_case()
+    w = r["topk_w"].astype(np.float64)
+    L = np.sum(g * O.combine(y, tok_row, w))
+    gy, gw = O.combine_backward(g, y, tok_row, w, y.shape[0])
+    assert abs(np.sum(gy * y) - L) <= 1e-9 * (1 + abs(L))
+    assert abs(np.sum(gw * w) - L) <= 1e-9 * (1 + abs(L))
+    # padding rows receive no gradient
+    assert not gy[row_src < 0].any()
+
+
+def test_combine_backward_finite_differences():
+    """Central differences of L through O.combine at sampled coordinates;
+    L is linear in each, so the difference quotient is exact up to
+    rounding."""
+    cfg, r, tok_row, row_src, y, g = _backward_case(5)
+    w = r["topk_w"].astype(np.float64)
+    gy, gw = O.combine_backward(g, y, tok_row, w, y.shape[0])
+    rng = np.random.default_rng(6)
+
+    def L(yy, ww):
+        return np.sum(g * O.combine(yy, tok_row, ww))
+    h = 0.5
+    for _ in range(12):
+        row = int(rng.choice(np.nonzero(row_src >= 0)[0]))
+        c = int(rng.integers(cfg.H))
+        yp, ym = y.copy(), y.copy()
+        yp[row, c] += h
+        ym[row, c] -= h
+        assert abs((L(yp, w) - L(ym, w)) / (2 * h) - gy[row, c]) < 1e-9
+        t, j = int(rng.integers(cfg.T)), int(rng.integers(cfg.k))
+        wp, wm = w.copy(), w.copy()
+        wp[t, j] += h
+        wm[t, j] -= h
+        assert abs((L(y, wp) - L(y, wm)) / (2 * h) - gw[t, j]) < 1e-9
+
+
+def test_dispatch_backward_is_transpose_of_row_copy():
+    """<G, D(x)> = <D^T G, x> with D the row copy of the pinned
+    O.dispatch_rows (exact payload)."""
+    cfg, r, tok_row, row_src, y, g = _backward_case(7)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
+    rows, _ = O.dispatch_rows(x, row_src, "f32")
+    G = rng.standard_normal(rows.shape)
+    lhs = np.sum(G * np.asarray(rows, np.float64))
+    rhs = np.sum(O.dispatch_backward(G, tok_row) * x.astype(np.float64))
+    assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs))
+    # k = 1 with an identity plan: the gradient is the row itself
+    gx = O.dispatch_backward(G, tok_row[:, :1])
+    assert np.array_equal(gx, G[tok_row[:, 0]])
+
+
 # ------------------------------------------------------------------ workloads
 
 def test_zipf_bias_load_ratio():
