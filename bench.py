@@ -143,6 +143,147 @@ def cpu_baseline(cfg, wl, n_tokens):
     }
 
 
+def _mean_ms(pairs):
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
+def measure_cold(step, stream, dev, iters=10, flush_mb=1024):
+    """Per-stage times with the caches (L2 and the 256 MB MALL) flushed
+    before every iteration by writing flush_mb MiB of scratch."""
+    import torch
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
+    evs = []
+    for i in range(iters):
+        flush.fill_(i & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    del flush
+    return {
+        "route_us": round(_mean_ms([(e[0], e[1]) for e in evs]) * 1e3, 2),
+        "dispatch_us": round(_mean_ms([(e[1], e[2]) for e in evs]) * 1e3, 2),
+        "combine_us": round(_mean_ms([(e[2], e[3]) for e in evs]) * 1e3, 2),
+        "iters": iters, "flush_mib": flush_mb,
+    }
+
+
+def measure_backward(cfg, moe, y, tok_row, topk_w, stream, dev, iters=10):
+    """moe_combine_backward and moe_dispatch_backward through the forward
+    plan: times and achieved GB/s on their algorithmic bytes."""
+    import torch
+    T, H, k = cfg.T, cfg.H, cfg.k
+    S = T * k
+    by = 4 if cfg.y_dtype == "f32" else 2
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    g = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16)
+    grad_y = torch.zeros((y.shape[0], H), dtype=torch.bfloat16, device=dev)
+    grad_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    grad_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    sp = stream.cuda_stream
+
+    def once(ev=None):
+        if ev:
+            ev[0].record(stream)
+        moe.moe_combine_backward(g, y, tok_row, topk_w, grad_y, grad_w, sp)
+        if ev:
+            ev[1].record(stream)
+        moe.moe_dispatch_backward(grad_y, tok_row, grad_x, sp)
+        if ev:
+            ev[2].record(stream)
+    once()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(iters)]
+    for ev in evs:
+        once(ev)
+    torch.cuda.synchronize()
+    cb_us = _mean_ms([(e[0], e[1]) for e in evs]) * 1e3
+    db_us = _mean_ms([(e[1], e[2]) for e in evs]) * 1e3
+    cb_bytes = T * H * 2 + S * H * by + S * H * 2 + S * 8 + S * 4
+    db_bytes = S * H * 2 + T * H * 2 + S * 4
+    return {
+        "combine_backward_us": round(cb_us, 2),
+        "combine_backward_gbs": round(cb_bytes / (cb_us * 1e-6) / 1e9, 1),
+        "dispatch_backward_us": round(db_us, 2),
+        "dispatch_backward_gbs": round(db_bytes / (db_us * 1e-6) / 1e9, 1),
+        "bytes": {"combine_backward": cb_bytes, "dispatch_backward": db_bytes},
+        "grad_dtype": "bf16",
+    }
+
+
+def measure_farskip_overlap(cfg, moe, y, tok_row, topk_w, shared, resid,
+                            stream, dev, iters=10, n_next=2112):
+    """FarSkip split form on one GPU: the auxiliary residual stream first
+    (moe_farskip_aux), then the routed combine into the main stream on one
+    stream while a stand-in next-layer attention projection
+    (residual_no_routed @ W, [T, H] x [H, n_next] bf16, torch.matmul) runs on
+    a second stream of the same priority.  Reports each part alone, the two
+    in sequence and overlapped, and the combine time hidden."""
+    import torch
+    T, H = cfg.T, cfg.H
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    wq = (torch.randn((H, n_next), generator=gen, device=dev) /
+          float(np.sqrt(H))).to(torch.bfloat16)
+    rnr = torch.empty_like(resid)
+    res_out = torch.empty_like(resid)
+    q = torch.empty((T, n_next), dtype=torch.bfloat16, device=dev)
+    s2 = torch.cuda.Stream(device=dev)
+    sp = stream.cuda_stream
+
+    def aux():
+        moe.moe_farskip_aux(shared, resid, rnr, sp)
+
+    def main_combine():
+        moe.moe_combine_residual(y, tok_row, topk_w, shared, resid, res_out,
+                                 None, None, sp)
+
+    def gemm():
+        torch.matmul(rnr, wq, out=q)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        pairs = []
+        for _ in range(iters):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        return _mean_ms(pairs) * 1e3
+
+    def sequential():
+        aux()
+        main_combine()
+        gemm()
+
+    def overlapped():
+        aux()
+        ready = torch.cuda.Event()
+        ready.record(stream)
+        s2.wait_event(ready)
+        with torch.cuda.stream(s2):
+            gemm()
+        main_combine()
+        stream.wait_stream(s2)
+
+    t_aux, t_comb, t_gemm = timed(aux), timed(main_combine), timed(gemm)
+    t_seq, t_ovl = timed(sequential), timed(overlapped)
+    return {
+        "aux_us": round(t_aux, 2), "combine_main_us": round(t_comb, 2),
+        "next_gemm_us": round(t_gemm, 2),
+        "next_gemm": f"[{T},{H}] x [{H},{n_next}] bf16 (torch.matmul)",
+        "sequential_us": round(t_seq, 2), "overlapped_us": round(t_ovl, 2),
+        "hidden_us": round(t_seq - t_ovl, 2),
+        "hidden_frac_of_combine": round((t_seq - t_ovl) / t_comb, 3),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +293,12 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the backward and FarSkip-overlap measurements "
+                    "that follow the timed steps")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="also time the stages with L2 and MALL flushed "
+                    "before every iteration")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one plain device-to-device copy of this many "
                     "MiB before timing (reference for byte counters)")
@@ -291,6 +438,18 @@ def main():
             "traffic_unit": "bytes per launch (HBM read + write)",
         },
     }
+    dc = (d_ms + c_ms) * 1e3
+    line["dc_us_p10_p50_p90"] = [round(float(np.percentile(dc, q)), 2)
+                                 for q in (10, 50, 90)]
+    if args.cold_cache:
+        line["cold_cache"] = measure_cold(step, stream, dev)
+    if not args.no_extras:
+        line["backward"] = measure_backward(cfg, moe, y, d["tok_row"],
+                                            p["topk_w"], stream, dev)
+        if resid is not None:
+            line["farskip_overlap"] = measure_farskip_overlap(
+                cfg, moe, y, d["tok_row"], p["topk_w"], shared, resid,
+                stream, dev)
     if args.cpu_tokens > 0:
         line["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_tokens)
     print(json.dumps(line), flush=True)

@@ -269,17 +269,22 @@ hipError_t launch_farskip_aux(const void* shared, const void* residual,
 // One wave per token; each lane keeps k partial dot products over its
 // hidden elements, reduced across the wave in a fixed order at the end.
 template <int KMAX, int YT>
-__global__ __launch_bounds__(256) void combine_backward_kernel(
+__global__ __launch_bounds__(1024) void combine_backward_kernel(
     const unsigned char* __restrict__ g, const unsigned char* __restrict__ y,
     long long y_rows, int H, const int32_t* __restrict__ tok_row,
     const float* __restrict__ topk_w, int T, int k,
-    unsigned char* __restrict__ grad_y, float* __restrict__ grad_w) {
+    unsigned char* __restrict__ grad_y, float* __restrict__ grad_w, int hs) {
+  // hs waves of one workgroup share a token's hidden dimension (interleaved
+  // groups of 64 chunks); their partial dot products meet in LDS and are
+  // summed in wave order, so grad_w does not depend on timing.
+  __shared__ float part[16][KMAX];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wv;
-  if (t >= T) return;
+  const int tpb = (int)(blockDim.x >> 6) / hs;
+  const int t = blockIdx.x * tpb + wv / hs, p = wv % hs;
+  const bool live = t < T;
   int r = -1;
   float wt = 0.0f;
-  if (lane < k) {
+  if (live && lane < k) {
     const size_t s = (size_t)t * k + lane;
     r = tok_row[s];
     wt = topk_w[s];
@@ -295,12 +300,12 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
                     : 0.0f;
   }
   const size_t yrowb = (size_t)H * (YT == 1 ? 2 : 4);
-  const size_t trow = (size_t)t * H * 2;
-  const int nc8 = H / 8;
+  const size_t trow = (size_t)(live ? t : 0) * H * 2;
+  const int nc8 = live ? H / 8 : 0;
   float dot[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) dot[j] = 0.0f;
-  for (int c = lane; c < nc8; c += 64) {
+  for (int c = p * 64 + lane; c < nc8; c += hs * 64) {
     float gf[8];
     unpack8_bf16(ld16_stream(g + trow + (size_t)c * 16), gf);
 #pragma unroll
@@ -332,7 +337,13 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     float v = dot[j];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    if (lane == 0 && j < k) grad_w[(size_t)t * k + j] = v;
+    if (lane == 0) part[wv][j] = v;
+  }
+  __syncthreads();
+  if (live && p == 0 && lane < k) {
+    float v = 0.0f;
+    for (int q = 0; q < hs; ++q) v += part[wv + q][lane];
+    grad_w[(size_t)t * k + lane] = v;
   }
 }
 
@@ -342,7 +353,13 @@ hipError_t launch_combine_backward(const void* g, const void* y, int ydt,
                                    const float* topk_w, int T, int k,
                                    void* grad_y, float* grad_w,
                                    hipStream_t s) {
-  const dim3 grid((T + 3) / 4);
+  // waves per token: a power of two up to 16, enough for ~2048 waves
+  const int groups = (H / 8 + 63) / 64;
+  int hs = 1;
+  while (hs < 16 && 2 * hs <= groups && (long long)T * hs < 2048) hs *= 2;
+  const int waves = hs > 4 ? hs : 4;
+  const int tpb = waves / hs;
+  const dim3 grid((unsigned)((T + tpb - 1) / tpb)), block(64 * waves);
   const unsigned char* gb = (const unsigned char*)g;
   const unsigned char* yb = (const unsigned char*)y;
   unsigned char* dyb = (unsigned char*)grad_y;
@@ -350,11 +367,13 @@ hipError_t launch_combine_backward(const void* g, const void* y, int ydt,
 #define MOE_CBWD(KV)                                                           \
   do {                                                                         \
     if (ydt == DT_BF16)                                                        \
-      hipLaunchKernelGGL((combine_backward_kernel<KV, 1>), grid, dim3(256), 0, \
-                         s, gb, yb, yr, H, tok_row, topk_w, T, k, dyb, grad_w);\
+      hipLaunchKernelGGL((combine_backward_kernel<KV, 1>), grid, block, 0, s,  \
+                         gb, yb, yr, H, tok_row, topk_w, T, k, dyb, grad_w,    \
+                         hs);                                                  \
     else                                                                       \
-      hipLaunchKernelGGL((combine_backward_kernel<KV, 0>), grid, dim3(256), 0, \
-                         s, gb, yb, yr, H, tok_row, topk_w, T, k, dyb, grad_w);\
+      hipLaunchKernelGGL((combine_backward_kernel<KV, 0>), grid, block, 0, s,  \
+                         gb, yb, yr, H, tok_row, topk_w, T, k, dyb, grad_w,    \
+                         hs);                                                  \
   } while (0)
   if (k <= 1) MOE_CBWD(1);
   else if (k <= 2) MOE_CBWD(2);

@@ -75,8 +75,11 @@ def _check_grad_y(gpu_bits, exact):
 
 
 def _check_grad_w(gpu, exact, g, yrows, H):
-    """fp32 dot product over H: each lane sums H/64 products in order, then
-    a 6-level butterfly, so |err| <= (H/64 + 8) u sum|g_h y_h|."""
+    """fp32 dot product over H: a lane sums at most H/(64 w) + 8 products in
+    order (w waves share the token), then a 6-level lane butterfly and an
+    in-order sum of the w partials; for the w the launcher picks this is at
+    most H/64 + 8 roundings on the way, so |err| <= (H/64 + 8) u
+    sum|g_h y_h|."""
     mag = np.abs(g[:, None, :] * yrows).sum(axis=2)
     bound = (H / 64 + 8) * U * mag + 1e-30
     err = np.abs(np.asarray(gpu, np.float64) - exact)
