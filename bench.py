@@ -291,7 +291,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dsv3_prefill")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens in the CPU-oracle baseline sample (0 = skip)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the backward and FarSkip-overlap measurements "
