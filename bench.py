@@ -213,6 +213,62 @@ def measure_backward(cfg, moe, y, tok_row, topk_w, stream, dev, iters=10):
     }
 
 
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA peak, TFLOP/s
+
+
+def measure_expert_gemm(cfg, moe, d, p, dev, iters=5):
+    """The fp8 grouped expert GEMM (moe_expert_gemm_fp8) on the dispatched
+    fp8 buffer: every expert maps H -> H with synthetic E4M3 weights and
+    128x128 block scales generated on the device.  FLOPs count the T*k
+    routed rows (the padded rows the kernel also computes are reported
+    separately)."""
+    import torch
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    N = K = H
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(13)
+    w = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        # exponent field <= 7 (magnitudes <= 1.875): no NaN codes
+        w[e] = torch.randint(0, 256, (N, K), generator=gen, device=dev,
+                             dtype=torch.uint8) & 0xBF
+    w_scales = (torch.rand((E, N // 128, K // 128), generator=gen,
+                           device=dev) + 0.5) / float(np.sqrt(K))
+    cap = d["rows"].shape[0]
+    y = torch.empty((cap, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moe.moe_expert_gemm_workspace_bytes(cap, E),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def once():
+        moe.moe_expert_gemm_fp8(d["rows"], d["row_scales"], d["row_src"],
+                                p["offsets"], w, w_scales, y, ws,
+                                stream.cuda_stream)
+    once()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        once()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    us = _mean_ms(pairs) * 1e3
+    R = int(p["offsets"][-1].item())
+    flop = 2.0 * T * k * N * K
+    tf = flop / (us * 1e-6) / 1e12
+    del w, y
+    return {
+        "us": round(us, 1), "tflops": round(tf, 1),
+        "tflops_padded_rows": round(2.0 * R * N * K / (us * 1e-6) / 1e12, 1),
+        "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+        "shape": f"{E} experts x [{R} padded rows ({T * k} routed), K={K}] "
+                 f"x [K, N={N}] fp8 -> bf16",
+    }
+
+
 def measure_farskip_overlap(cfg, moe, y, tok_row, topk_w, shared, resid,
                             stream, dev, iters=10, n_next=2112):
     """FarSkip split form on one GPU: the auxiliary residual stream first
@@ -443,6 +499,8 @@ def main():
                                  for q in (10, 50, 90)]
     if args.cold_cache:
         line["cold_cache"] = measure_cold(step, stream, dev)
+    if not args.no_extras and cfg.payload == "fp8":
+        line["expert_gemm"] = measure_expert_gemm(cfg, moe, d, p, dev)
     if not args.no_extras:
         line["backward"] = measure_backward(cfg, moe, y, d["tok_row"],
                                             p["topk_w"], stream, dev)

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "expert_gemm.h"
 #include "moe_launch.h"
 
 namespace {
@@ -322,6 +323,53 @@ int moe_dispatch_backward(const void* grad_rows, int rows_dtype, int H,
                                         nullptr, nullptr, nullptr, nullptr,
                                         grad_x, grad_x_dtype,
                                         (hipStream_t)stream));
+}
+
+size_t moe_expert_gemm_workspace_bytes(size_t rows_capacity, int E) {
+  if (E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  return moe::gemm_workspace_bytes(rows_capacity, E);
+}
+
+int moe_expert_gemm_fp8(const void* rows, const float* row_scales, int K,
+                        size_t rows_capacity, const int32_t* row_src,
+                        const int32_t* offsets, int E, const void* w,
+                        const float* w_scales, int N, void* y, int y_dtype,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (K < 128 || K % 128 != 0 || K > moe::kGemmMaxK || N < 128 ||
+      N % 128 != 0 || E < 1 || E > MOE_MAX_EXPERTS ||
+      rows_capacity > (size_t)0x7fffffff)
+    return MOE_ERR_SHAPE;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (rows_capacity == 0) return MOE_OK;
+  if (rows == nullptr || row_scales == nullptr || offsets == nullptr ||
+      w == nullptr || w_scales == nullptr || y == nullptr ||
+      workspace == nullptr)
+    return MOE_ERR_NULL;
+  if (workspace_bytes < moe::gemm_workspace_bytes(rows_capacity, E))
+    return MOE_ERR_WORKSPACE;
+  if (!aligned(rows, 16) || !aligned(w, 16) || !aligned(y, 16) ||
+      !aligned(workspace, 16) || !aligned(row_scales, 4) ||
+      !aligned(w_scales, 4) || !aligned(offsets, 4) || !aligned(row_src, 4))
+    return MOE_ERR_ALIGN;
+  const size_t kb = (size_t)K / 128;
+  const Span ins[] = {{rows, rows_capacity * K},
+                      {row_scales, rows_capacity * kb * 4},
+                      {row_src, row_src ? rows_capacity * 4 : 0},
+                      {offsets, (size_t)(E + 1) * 4},
+                      {w, (size_t)E * N * K},
+                      {w_scales, (size_t)E * (N / 128) * kb * 4}};
+  const Span outs[] = {
+      {y, rows_capacity * N * dtype_size(y_dtype)},
+      {workspace, moe::gemm_workspace_bytes(rows_capacity, E)}};
+  if (any_overlap(outs, 2, ins, 6) || overlap(outs[0], outs[1]))
+    return MOE_ERR_ALIAS;
+  if (trace_on())
+    std::fprintf(stderr, "moe_expert_gemm_fp8 cap=%zu K=%d N=%d E=%d\n",
+                 rows_capacity, K, N, E);
+  return hip_status(moe::launch_expert_gemm(
+      rows, row_scales, K, rows_capacity, row_src, offsets, E, w, w_scales, N,
+      y, y_dtype, workspace, (hipStream_t)stream));
 }
 
 int moe_expert_fixture(const void* rows, int payload_dtype,

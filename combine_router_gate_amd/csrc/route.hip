@@ -456,7 +456,12 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 template <int EPW, int TT, int PQ, int D>
 __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, float* __restrict__ partial) {
+    int H, int E, int KR, float* __restrict__ partial,
+    unsigned* __restrict__ done) {
+  // the completion counter of the reduction launched next on this stream
+  if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 &&
+      threadIdx.x == 0)
+    *done = 0u;
   constexpr int EP = 64 * EPW;             // padded experts
   constexpr int TTOK = 16 * TT;            // tokens of the workgroup
   constexpr int KS = 32 * PQ;              // k per super-step
@@ -843,15 +848,189 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
   }
 }
 
+// ------------------------------------------------------------------ small batches
+
+// Histogram, padded scan, first rows and ranks of all T <= kSmallPlanT
+// tokens in one workgroup of NT threads (the same results as
+// tile_histogram_kernel followed by expert_scan_kernel).  bits: LDS
+// [ceil(T/64) * E] 64-bit tile ballots; ecnt: LDS [E].
+template <int NT>
+__device__ void small_plan(const int32_t* __restrict__ topk_idx, int T, int k,
+                           int E, int pad, int32_t* __restrict__ counts,
+                           int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ tile_base,
+                           int32_t* __restrict__ slot_rank,
+                           unsigned long long* bits, int* ecnt) {
+  const int tid = threadIdx.x;
+  const int nt = (T + 63) / 64;
+  for (int i = tid; i < nt * E; i += NT) bits[i] = 0ull;
+  __syncthreads();
+  const int n = T * k;
+  for (int p = tid; p < n; p += NT) {
+    const int e = topk_idx[p];
+    const int t = p / k;
+    if (e >= 0 && e < E) atomicOr(&bits[(t >> 6) * E + e], 1ull << (t & 63));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int c = 0;
+    for (int q = 0; q < nt; ++q) c += __popcll(bits[q * E + e]);
+    counts[e] = c;
+    ecnt[e] = (c + pad - 1) / pad * pad;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive scan of the padded counts: lane l owns experts [8l, 8l+8)
+    constexpr int PER = MOE_MAX_EXPERTS / 64;
+    int loc[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid * PER + i;
+      loc[i] = e < E ? ecnt[e] : 0;
+      sum += loc[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (tid >= off) incl += o;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid * PER + i;
+      if (e < E) {
+        ecnt[e] = run;
+        offsets[e] = run;
+      }
+      run += loc[i];
+    }
+    if (tid == 63) offsets[E] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int run = ecnt[e];
+    for (int q = 0; q < nt; ++q) {
+      tile_base[(size_t)q * E + e] = run;
+      run += __popcll(bits[q * E + e]);
+    }
+  }
+  for (int p = tid; p < n; p += NT) {
+    const int e = topk_idx[p];
+    const int t = p / k;
+    int r = -1;
+    if (e >= 0 && e < E)
+      r = __popcll(bits[(t >> 6) * E + e] & ((1ull << (t & 63)) - 1ull));
+    slot_rank[p] = r;
+  }
+}
+
+// moe_plan for few tokens: one workgroup instead of histogram + scan.
+__global__ __launch_bounds__(512) void plan_small_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int k, int E, int pad,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank) {
+  __shared__ unsigned long long bits[(kSmallPlanT / 64) * MOE_MAX_EXPERTS];
+  __shared__ int ecnt[MOE_MAX_EXPERTS];
+  small_plan<512>(topk_idx, T, k, E, pad, counts, offsets, tile_base,
+                  slot_rank, bits, ecnt);
+}
+
+// Reduction of the split gate for few tokens.  A workgroup of RW waves
+// covers 4 tokens (16 lanes each); wave w adds the ranges w, w + RW, ... in
+// ascending order, then wave 0 adds the RW wave sums in wave order (fixed
+// order: the logits do not depend on timing) and selects the top-k.  Each
+// workgroup then publishes its results (device-scope fence) and counts
+// itself done; the last one builds the plan of all tokens.  The counter is
+// zeroed by gate_partial_kernel, which precedes this kernel on the stream.
+template <int ET, int RW>
+__global__ __launch_bounds__(64 * RW) void gate_reduce_plan_small_kernel(
+    const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
+    int pad, const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ logits_dbg,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank,
+    unsigned* __restrict__ done) {
+  constexpr int NT = 64 * RW;
+  constexpr int B = ET <= 16 ? 4 : 2;           // ranges in flight per wave
+  constexpr int RED = RW * 4 * 16 * ET;         // floats of wave sums
+  constexpr int BITS = (kSmallPlanT / 64) * MOE_MAX_EXPERTS;
+  constexpr int LDS64 = RED / 2 > BITS ? RED / 2 : BITS;
+  __shared__ unsigned long long lds[LDS64];
+  __shared__ int ecnt[MOE_MAX_EXPERTS];
+  __shared__ int last;
+  float* red = (float*)lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t = blockIdx.x * 4 + g;
+  const int tc = t < T ? t : T - 1;
+
+  float v[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et) v[et] = 0.0f;
+  for (int q0 = wv; q0 < S; q0 += B * RW) {
+    float u[B][ET];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int q = q0 + b * RW < S ? q0 + b * RW : q0;
+      const float* pq = partial + ((size_t)q * T + tc) * EPS;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const int e = et * 16 + c16;
+        u[b][et] = pq[e < E ? e : 0];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      if (q0 + b * RW < S) {
+#pragma unroll
+        for (int et = 0; et < ET; ++et) v[et] += u[b][et];
+      }
+  }
+#pragma unroll
+  for (int et = 0; et < ET; ++et)
+    red[((wv * 4 + g) * ET + et) * 16 + c16] = v[et];
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      float a = red[(g * ET + et) * 16 + c16];
+      for (int w = 1; w < RW; ++w) a += red[((w * 4 + g) * ET + et) * 16 + c16];
+      const int e = et * 16 + c16;
+      a += (bias != nullptr && e < E) ? bias[e] : 0.0f;
+      if (logits_dbg != nullptr && t < T && e < E)
+        logits_dbg[(size_t)t * E + e] = a;
+      v[et] = a;
+    }
+    topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w);
+  }
+  // release this workgroup's top-k, count it done; the last one acquires
+  // every other workgroup's results before planning
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  small_plan<NT>(topk_idx, T, k, E, pad, counts, offsets, tile_base,
+                 slot_rank, lds, ecnt);
+}
+
 // ------------------------------------------------------------------ launchers
+
+// What remains of moe_route after the gate kernels.
+enum { kRouteNeedPlan = 0, kRouteNeedScan = 1, kRouteDone = 2 };
 
 template <typename XT>
 static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
-                                    int T, int H, int E, int k, int32_t* idx,
-                                    float* tw, float* dbg, int32_t* tb,
-                                    int32_t* sr, bool* fused_hist,
+                                    int T, int H, int E, int k, int pad,
+                                    int32_t* idx, float* tw, float* dbg,
+                                    int32_t* counts, int32_t* offsets,
+                                    int32_t* tb, int32_t* sr, int* stage,
                                     hipStream_t s) {
-  *fused_hist = false;
+  *stage = kRouteNeedPlan;
   const int et = (E + 15) / 16;
   if (et <= 2) {
     const dim3 grid((T + 15) / 16);
@@ -880,10 +1059,15 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       const int KR = ((H + S - 1) / S + 63) / 64 * 64;
       S = (H + KR - 1) / KR;
       float* part = (float*)((unsigned char*)sr + ws_rank_bytes(T, k));
+      const bool small = T <= kSmallPlanT;
+      unsigned* done =
+          small ? (unsigned*)((unsigned char*)part + ws_partial_bytes(T, E) -
+                              256)
+                : nullptr;
       const dim3 pgrid(tiles, S);
 #define MOE_GATE_PART(EPWV, TTV, DV)                                           \
   hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV>), pgrid,          \
-                     dim3(256), 0, s, x, w, T, H, E, KR, part)
+                     dim3(256), 0, s, x, w, T, H, E, KR, part, done)
 #define MOE_GATE_PART_E(TTV)                                                   \
   do {                                                                         \
     if (epw == 1) MOE_GATE_PART(1, TTV, 4);                                    \
@@ -906,6 +1090,23 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
       const int EPS = 64 * epw;
+      if (small) {
+        // one kernel: reduction, top-k, and in its last workgroup the
+        // histogram, scan and ranks of all tokens
+        const dim3 rgrid((T + 3) / 4);
+#define MOE_GATE_SMALL(ETV)                                                    \
+  hipLaunchKernelGGL((gate_reduce_plan_small_kernel<ETV, 8>), rgrid,          \
+                     dim3(512), 0, s, part, S, EPS, T, E, k, pad, bias, idx,  \
+                     tw, dbg, counts, offsets, tb, sr, done)
+        if (epw == 1) MOE_GATE_SMALL(4);
+        else if (epw == 2) MOE_GATE_SMALL(8);
+        else if (epw == 4) MOE_GATE_SMALL(16);
+        else if (epw == 6) MOE_GATE_SMALL(24);
+        else MOE_GATE_SMALL(32);
+#undef MOE_GATE_SMALL
+        *stage = kRouteDone;
+        return hipGetLastError();
+      }
       // reduction: 64-token workgroups (fused histogram) for many tokens,
       // 16-token workgroups for few
       const bool fuse = T >= 1024;
@@ -926,7 +1127,7 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       else MOE_GATE_RED_E(32, 4, 4);
 #undef MOE_GATE_RED_E
 #undef MOE_GATE_RED
-      *fused_hist = fuse;
+      *stage = fuse ? kRouteNeedScan : kRouteNeedPlan;
       return hipGetLastError();
     }
 #define MOE_GATE_V2(EPWV, PQV, DV)                                         \
@@ -938,7 +1139,7 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     else if (epw == 6) MOE_GATE_V2(6, 2, 3);
     else MOE_GATE_V2(8, 2, 2);
 #undef MOE_GATE_V2
-    *fused_hist = true;
+    *stage = kRouteNeedScan;
     return hipGetLastError();
   }
 #define MOE_GATE_WIDE(ETV)                                                    \
@@ -975,19 +1176,21 @@ hipError_t launch_route(const void* x, const void* w, int xdt,
   int32_t* tile_base = (int32_t*)workspace;
   int32_t* slot_rank =
       (int32_t*)((unsigned char*)workspace + ws_tile_bytes(T, E));
-  bool fused = false;
+  int stage = kRouteNeedPlan;
   hipError_t err;
   if (xdt == DT_BF16)
     err = launch_gate_typed<uint16_t>((const uint16_t*)x, (const uint16_t*)w,
-                                      bias, T, H, E, k, topk_idx, topk_w,
-                                      logits_dbg, tile_base, slot_rank,
-                                      &fused, s);
+                                      bias, T, H, E, k, pad, topk_idx, topk_w,
+                                      logits_dbg, counts, offsets, tile_base,
+                                      slot_rank, &stage, s);
   else
     err = launch_gate_typed<float>((const float*)x, (const float*)w, bias, T,
-                                   H, E, k, topk_idx, topk_w, logits_dbg,
-                                   tile_base, slot_rank, &fused, s);
+                                   H, E, k, pad, topk_idx, topk_w, logits_dbg,
+                                   counts, offsets, tile_base, slot_rank,
+                                   &stage, s);
   if (err != hipSuccess) return err;
-  if (!fused)
+  if (stage == kRouteDone) return hipSuccess;
+  if (stage == kRouteNeedPlan)
     return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
   return launch_scan(tile_base, num_tiles(T), E, pad, counts, offsets, s);
 }
@@ -999,6 +1202,11 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
   int32_t* tile_base = (int32_t*)workspace;
   int32_t* slot_rank =
       (int32_t*)((unsigned char*)workspace + ws_tile_bytes(T, E));
+  if (nt > 0 && T <= kSmallPlanT) {
+    hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(512), 0, s, topk_idx,
+                       T, k, E, pad, counts, offsets, tile_base, slot_rank);
+    return hipGetLastError();
+  }
   if (nt > 0) {
     hipLaunchKernelGGL(tile_histogram_kernel, dim3(nt), dim3(256), 0, s,
                        topk_idx, T, k, E, tile_base, slot_rank);

@@ -27,6 +27,7 @@ import numpy as np
 
 TID_X, TID_W, TID_PERM, TID_SIGMA, TID_SHARED, TID_RESID = 1, 2, 3, 4, 5, 6
 TID_GRAD = 7
+TID_WCODE, TID_WSCALE = 8, 9
 
 # Zipf exponent of the skewed workload and the strength with which its
 # log-probabilities enter the router logits.  0.17 gives a max/mean expert
@@ -197,3 +198,25 @@ def grad_tensor(seed: int, shape, dtype: str = "bf16", std: float = 1.0,
     ``dtype``.  ``stream`` separates several gradients of one seed."""
     return _pack(_normal(seed, TID_GRAD * 1000 + stream, tuple(shape), std),
                  dtype)
+
+
+def expert_weights_fp8(seed: int, E: int, N: int, K: int,
+                       experts=None):
+    """Synthetic fp8 expert weights for the grouped GEMM: E4M3 codes [E, N, K]
+    (uint8) with a random sign, exponent field uniform in 4..9 and random
+    mantissa (magnitudes 2^-3 .. 7.5, never NaN), and block scales
+    [E, N/128, K/128] float32 uniform in [0.5, 1.5] / sqrt(K).  With
+    ``experts`` given, only those experts get random codes (drawn from a
+    generator seeded by the expert id) and the others are zero."""
+    codes = np.zeros((E, N, K), dtype=np.uint8)
+    scales = (_rng(seed, TID_WSCALE).uniform(0.5, 1.5, size=(E, N // 128,
+                                                             K // 128))
+              / np.sqrt(K)).astype(np.float32)
+    todo = range(E) if experts is None else experts
+    for e in todo:
+        g = _rng(seed, TID_WCODE * 100000 + int(e))
+        sign = g.integers(0, 2, size=(N, K), dtype=np.uint8)
+        expo = g.integers(4, 10, size=(N, K), dtype=np.uint8)
+        mant = g.integers(0, 8, size=(N, K), dtype=np.uint8)
+        codes[e] = (sign << 7) | (expo << 3) | mant
+    return codes, scales

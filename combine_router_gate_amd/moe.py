@@ -44,6 +44,9 @@ _SIGS = {
     "moe_expert_fixture": (_i, [_vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz,
                                 _vp, _i, _vp]),
     "moe_farskip_aux": (_i, [_vp, _vp, _vp, _i, _i, _vp]),
+    "moe_expert_gemm_workspace_bytes": (_sz, [_sz, _i]),
+    "moe_expert_gemm_fp8": (_i, [_vp, _vp, _i, _sz, _vp, _vp, _i, _vp, _vp,
+                                 _i, _vp, _i, _vp, _sz, _vp]),
     "moe_combine_backward": (_i, [_vp, _vp, _i, _i, _sz, _vp, _vp, _i, _i,
                                   _vp, _vp, _vp]),
     "moe_dispatch_backward": (_i, [_vp, _i, _i, _sz, _vp, _i, _i, _vp, _i,
@@ -185,6 +188,22 @@ def moe_expert_fixture(rows, payload_dtype, row_scales, row_src, offsets,
         _ptr(offsets), E, _ptr(sigma), rows.shape[0], _ptr(y), _dt(y),
         stream if stream is not None else _stream(y.device))
     _check(st, "moe_expert_fixture")
+
+
+def moe_expert_gemm_workspace_bytes(rows_capacity: int, E: int) -> int:
+    return lib().moe_expert_gemm_workspace_bytes(rows_capacity, E)
+
+
+def moe_expert_gemm_fp8(rows, row_scales, row_src, offsets, w, w_scales, y,
+                        workspace, stream=None):
+    cap, K = rows.shape
+    E, N = w.shape[0], w.shape[1]
+    st = lib().moe_expert_gemm_fp8(
+        _ptr(rows), _ptr(row_scales), K, cap, _ptr(row_src), _ptr(offsets), E,
+        _ptr(w), _ptr(w_scales), N, _ptr(y), _dt(y), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0,
+        stream if stream is not None else _stream(rows.device))
+    _check(st, "moe_expert_gemm_fp8")
 
 
 def moe_farskip_aux(shared, residual_in, residual_no_routed, stream=None):
@@ -348,3 +367,19 @@ def dispatch_backward(grad_rows, tok_row, out_dtype=torch.float32):
                          device=grad_rows.device)
     moe_dispatch_backward(grad_rows, tok_row, grad_x)
     return grad_x
+
+
+def expert_gemm_fp8(d: Dict[str, torch.Tensor], p: Dict[str, torch.Tensor],
+                    w: torch.Tensor, w_scales: torch.Tensor,
+                    y_dtype=torch.bfloat16) -> torch.Tensor:
+    """Grouped fp8 GEMM over the dispatched rows: y [rows_capacity, N].
+    w: [E, N, K] uint8 E4M3 codes, w_scales: [E, N/128, K/128] fp32."""
+    rows = d["rows"]
+    cap = rows.shape[0]
+    E, N = w.shape[0], w.shape[1]
+    y = torch.empty((cap, N), dtype=y_dtype, device=rows.device)
+    ws = torch.empty(max(moe_expert_gemm_workspace_bytes(cap, E), 1),
+                     dtype=torch.uint8, device=rows.device)
+    moe_expert_gemm_fp8(rows, d["row_scales"], d["row_src"], p["offsets"], w,
+                        w_scales, y, ws)
+    return y

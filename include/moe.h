@@ -16,6 +16,9 @@
  *   moe_farskip_aux      the auxiliary residual stream alone (split form)
  *   moe_combine_backward, moe_dispatch_backward
  *                        gradients through the same routing plan
+ *   moe_expert_gemm_fp8  fp8 grouped GEMM of every expert over its segment
+ *                        of the dispatched buffer (1x128 activation scales,
+ *                        128x128 weight blocks)
  *   moe_expert_fixture   a stand-in expert (y = sigma_e * row) for tests and
  *                        benchmarks; not part of the transform
  *
@@ -275,6 +278,37 @@ int moe_dispatch_backward(const void* grad_rows, int rows_dtype, int H,
                           size_t rows_capacity, const int32_t* tok_row, int T,
                           int k, void* grad_x, int grad_x_dtype,
                           void* stream);
+
+/*
+ * moe_expert_gemm_fp8 -- grouped GEMM of every expert over its segment of
+ * the fp8 expert-major buffer, in the form dispatch writes it (the grouped
+ * GEMM between dispatch and combine: "Efficient and Portable
+ * Mixture-of-Experts Communication", Dispatch; FP8 tokens with block scaling
+ * factors: DeepEP news, technical overview).  For every row r of expert e's
+ * segment [offsets[e], offsets[e+1]) and every n < N:
+ *   y[r, n] = sum_b row_scales[r, b] * w_scales[e, n/128, b]
+ *             * sum_{h = 128b}^{128b+127} E4M3(rows[r, h]) * E4M3(w[e, n, h])
+ * in fp32 (each 128-wide block's fp8 products summed by the matrix core, then
+ * scaled and added in block order), stored as fp32 or rounded once to bf16.
+ *   rows       [rows_capacity, K] OCP E4M3 codes; row_scales [rows_capacity,
+ *              K/128] fp32 (moe_dispatch's fp8 output)
+ *   row_src    [rows_capacity] int32 or NULL: rows with row_src < 0 (padding)
+ *              are stored as zeros
+ *   offsets    [E+1] int32 from moe_route / moe_plan (device)
+ *   w          [E, N, K] E4M3 codes; w_scales [E, N/128, K/128] fp32
+ *   y          [rows_capacity, N] y_dtype (MOE_BF16 or MOE_F32); rows outside
+ *              every segment are not written
+ *   workspace  >= moe_expert_gemm_workspace_bytes(rows_capacity, E) bytes
+ * K and N multiples of 128, K <= 8192.  Segment bounds are clamped to
+ * rows_capacity.
+ */
+size_t moe_expert_gemm_workspace_bytes(size_t rows_capacity, int E);
+int moe_expert_gemm_fp8(const void* rows, const float* row_scales, int K,
+                        size_t rows_capacity, const int32_t* row_src,
+                        const int32_t* offsets, int E, const void* w,
+                        const float* w_scales, int N, void* y, int y_dtype,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * moe_expert_fixture -- stand-in expert used by tests and benchmarks in

@@ -279,6 +279,28 @@ def expert_fixture_row(row, scales, sigma_e, payload: str, y_dtype: str):
     return bf16_bits(round_to_bf16(y))
 
 
+def expert_gemm_fp8(rows, row_scales, w_codes, w_scales, e: int):
+    """fp8 grouped GEMM of expert e over the given rows of its segment
+    (the expert GEMM between dispatch and combine: Perplexity page,
+    Dispatch; FP8 tokens with block scaling factors: DeepEP news, technical
+    overview).  Each 128-wide block b contributes its exact sum of decoded
+    products times the block's two scales:
+      y[r, n] = sum_b sa[r, b] * sw[e, n // 128, b]
+                * sum_{h in b} E4M3(rows[r, h]) * E4M3(w[e, n, h])
+    rows: [m, K] codes, row_scales: [m, K/128]; float64 result [m, N]."""
+    a = e4m3_decode(rows)
+    wd = e4m3_decode(w_codes[e])
+    sa = np.asarray(row_scales, dtype=np.float64)
+    sw = np.asarray(w_scales[e], dtype=np.float64)
+    m, K = a.shape
+    N = wd.shape[0]
+    y = np.zeros((m, N), dtype=np.float64)
+    for b in range(K // 128):
+        part = a[:, 128 * b:128 * (b + 1)] @ wd[:, 128 * b:128 * (b + 1)].T
+        y += sa[:, b:b + 1] * part * np.repeat(sw[:, b], 128)[None, :]
+    return y
+
+
 def expert_of_row(offsets, r: int) -> int:
     """Expert whose padded segment [offsets[e], offsets[e+1]) holds row r."""
     return int(np.searchsorted(np.asarray(offsets), r, side="right") - 1)

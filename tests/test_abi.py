@@ -228,3 +228,34 @@ def test_dispatch_backward_validation(L, no_gpu):
     assert call(gx=A[2] + 8) == ALIGN
     assert call(gx=A[0] + 256) == ALIAS
     assert call(gx=A[1]) == ALIAS
+
+
+def test_expert_gemm_validation(L, no_gpu):
+    cap = 1024
+    wsb = moe.moe_expert_gemm_workspace_bytes(cap, 8)
+    assert wsb >= 8 * (cap // 128 + 8)
+    assert moe.moe_expert_gemm_workspace_bytes(cap, 0) == 0
+
+    def call(**kw):
+        a = dict(rows=A[0], rsc=A[1], K=512, cap=cap, src=A[2], offs=A[3],
+                 E=8, w=A[4], wsc=A[5], N=256, y=A[6], ydt=1, ws=A[7],
+                 wsb=wsb)
+        a.update(kw)
+        return L.moe_expert_gemm_fp8(a["rows"], a["rsc"], a["K"], a["cap"],
+                                     a["src"], a["offs"], a["E"], a["w"],
+                                     a["wsc"], a["N"], a["y"], a["ydt"],
+                                     a["ws"], a["wsb"], None)
+    assert call(K=100) == SHAPE
+    assert call(K=8192 + 128) == SHAPE
+    assert call(N=200) == SHAPE
+    assert call(E=0) == SHAPE
+    assert call(ydt=2) == DTYPE
+    assert call(cap=0, rows=None) == OK
+    for name in ["rows", "rsc", "offs", "w", "wsc", "y", "ws"]:
+        assert call(**{name: None}) == NULL, name
+    assert call(wsb=wsb - 1) == WS
+    assert call(y=A[6] + 8) == ALIGN
+    assert call(rsc=A[1] + 2) == ALIGN
+    assert call(y=A[4]) == ALIAS
+    assert call(ws=A[6] + 256) == ALIAS
+    assert call(ws=A[3]) == ALIAS

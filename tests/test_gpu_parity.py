@@ -44,6 +44,12 @@ SMALL = {
     "split_t1500": C["dsv3_decode"].with_shape(T=1500, H=1024),
     "split_t3000_e128": C["dsv3_prefill"].with_shape(T=3000, H=512, E=128,
                                                      k=6, pad=32),
+    # few tokens: one-kernel reduction + plan, 24 and 32 expert tiles
+    "small_e384": C["moonep_skew"].with_shape(T=200),
+    "small_e512": C["moonep_skew"].with_shape(T=300, H=512, E=512,
+                                              zipf_bias=False),
+    "small_t512": C["dsv3_decode"].with_shape(T=512, H=1024, k=6, pad=16),
+    "small_t1": C["dsv3_decode"].with_shape(T=1, H=2048),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 

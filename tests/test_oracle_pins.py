@@ -494,6 +494,86 @@ def test_dispatch_backward_is_transpose_of_row_copy():
     assert np.array_equal(gx, G[tok_row[:, 0]])
 
 
+# ------------------------------------------------------------------ fp8 expert GEMM
+
+def _dequantized(codes, scales, rows_per_scale, cols_per_scale):
+    """Codes times their block scales, as one float64 matrix."""
+    v = O.e4m3_decode(codes)
+    s = np.repeat(np.repeat(np.asarray(scales, np.float64), rows_per_scale,
+                            axis=0), cols_per_scale, axis=1)
+    return v * s
+
+
+def test_expert_gemm_is_matmul_of_dequantized():
+    """Blockwise-scaled sums equal one library matmul of the dequantized
+    operands (1x128 activation blocks, 128x128 weight blocks)."""
+    rng = np.random.default_rng(21)
+    E, N, K, m = 3, 256, 384, 7
+    w, sw = I.expert_weights_fp8(5, E, N, K)
+    x = rng.standard_normal((m, K)).astype(np.float32) * 3
+    q, sa = zip(*[O.quantize_row_e4m3(x[i]) for i in range(m)])
+    q, sa = np.stack(q), np.stack(sa)
+    for e in range(E):
+        got = O.expert_gemm_fp8(q, sa, w, sw, e)
+        want = _dequantized(q, sa, 1, 128) @ _dequantized(w[e], sw[e], 128,
+                                                          128).T
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_expert_gemm_identity_weights_give_fixture():
+    """W_e = identity (code 1.0 on the diagonal) with scale sigma_e on the
+    diagonal blocks reproduces the scale expert: y = sigma_e * deq(row)."""
+    rng = np.random.default_rng(22)
+    K = N = 256
+    E = 2
+    w = np.zeros((E, N, K), np.uint8)
+    for e in range(E):
+        w[e][np.arange(N), np.arange(K)] = 0x38          # E4M3 1.0
+    sigma = np.array([0.75, 1.25], np.float32)
+    sw = np.ones((E, N // 128, K // 128), np.float32)
+    for e in range(E):
+        for b in range(K // 128):
+            sw[e, b, b] = sigma[e]
+    x = rng.standard_normal(K).astype(np.float32)
+    q, sa = O.quantize_row_e4m3(x)
+    for e in range(E):
+        y = O.expert_gemm_fp8(q[None], sa[None], w, sw, e)[0]
+        fix = O.expert_fixture_row(q, sa, sigma[e], "fp8", "f32")
+        np.testing.assert_allclose(y, fix.astype(np.float64), rtol=2 ** -22,
+                                   atol=0)
+
+
+def test_expert_gemm_integer_brute_force():
+    """Codes of small integers and unit scales: every output is an exact
+    integer, checked against Python integer sums."""
+    rng = np.random.default_rng(23)
+    ints = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, -1: 0xB8, -2: 0xC0}
+    keys = np.array(list(ints))
+    E, N, K, m = 2, 128, 256, 3
+    wv = rng.choice(keys, size=(E, N, K))
+    av = rng.choice(keys, size=(m, K))
+    enc = np.vectorize(lambda v: ints[int(v)])
+    w = enc(wv).astype(np.uint8)
+    q = enc(av).astype(np.uint8)
+    sw = np.ones((E, 1, K // 128), np.float32)
+    sa = np.ones((m, K // 128), np.float32)
+    for e in range(E):
+        y = O.expert_gemm_fp8(q, sa, w, sw, e)
+        for i in range(m):
+            for n in range(0, N, 17):
+                want = sum(int(av[i, h]) * int(wv[e, n, h]) for h in range(K))
+                assert y[i, n] == want
+
+
+def test_expert_weights_never_nan():
+    w, sw = I.expert_weights_fp8(1, 2, 128, 256)
+    v = O.e4m3_decode(w)
+    assert np.isfinite(v).all()
+    assert 0.125 <= np.abs(v).min() and np.abs(v).max() <= 7.5
+    w2, _ = I.expert_weights_fp8(1, 4, 128, 128, experts=[2])
+    assert not w2[[0, 1, 3]].any() and w2[2].any()
+
+
 # ------------------------------------------------------------------ workloads
 
 def test_zipf_bias_load_ratio():
