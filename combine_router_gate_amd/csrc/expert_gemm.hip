@@ -21,11 +21,12 @@
 //  * The weight tile is the instruction's first operand, so each lane ends
 //    up with 4 consecutive output columns of one row: one row scale per
 //    lane and block, 8-byte bf16 stores.
-//  * A workgroup computes a 128x128 tile (4 waves of 64x64, 16 MFMAs per
-//    block), operands loaded straight into registers one block ahead.
-//  * Work order is XCD-aware: consecutive tiles (8 column tiles of one row
-//    tile, then the next row tile) are given to workgroups of the same XCD,
-//    which then share operands in that XCD's L2.
+//  * A workgroup computes a 128x256 tile with 8 waves (two per SIMD, 64x64
+//    each); operands are staged through LDS in MFMA fragment order
+//    (conflict-free 16-byte reads), three blocks deep, loaded through
+//    registers (direct global->LDS copies measured slower on this part).
+//  * Work order: all column tiles of one row tile are consecutive, so the
+//    row tile's activations stay cached while the expert's weights stream.
 //  * Row tiles come from a tile map built on the device from offsets, so no
 //    count ever returns to the host.
 
@@ -207,6 +208,232 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_fp8_kernel(
   }
 }
 
+// ------------------------------------------------------------------ v2
+
+// Direct global -> LDS copy of 16 (or 4) bytes per lane; lane i's data lands
+// at lds + i * bytes (gfx950 global_load_lds_dwordx4 / _dword).
+__device__ __forceinline__ void dma16(const unsigned char* g, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds(
+      (const void __attribute__((address_space(1)))*)g,
+      (void __attribute__((address_space(3)))*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const float* g, float* l) {
+  __builtin_amdgcn_global_load_lds(
+      (const void __attribute__((address_space(1)))*)g,
+      (void __attribute__((address_space(3)))*)l, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A workgroup computes a 128 (rows) x 256 (columns) tile with 8 waves (two
+// per SIMD); wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64,
+// i.e. 4 x 4 MFMA tiles.  Per 128-wide block each wave copies, straight into
+// LDS, one row group of the activation tile, two of the weight tile (16 rows
+// x 128 bytes each, in MFMA fragment order so every ds_read_b128 is
+// conflict-free) and 64 row scales; three blocks are in flight.  A block's 16
+// MFMAs are issued back to back into separate result registers, then their
+// results are scaled into the fp32 accumulators, so one wave's scaling runs
+// while the other wave's MFMAs occupy the matrix core.
+constexpr int kV2TM = 128, kV2TN = 256, kV2Stages = 3;
+constexpr int kV2A = kV2TM * 128, kV2B = kV2TN * 128;
+constexpr int kV2Scales = 8 * 64 * 4;                    // 64 rows per wave
+constexpr int kV2Stage = kV2A + kV2B + kV2Scales;
+constexpr int kV2DmaPerWave = 1 * 2 + 2 * 2 + 1;
+
+template <int YT, int ORDER, int VIA_REGS>
+__global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
+    const unsigned char* __restrict__ rows, const float* __restrict__ rscale,
+    int K, int cap, const int32_t* __restrict__ row_src,
+    const int32_t* __restrict__ offsets, const unsigned char* __restrict__ w,
+    const float* __restrict__ wscale, int N, unsigned char* __restrict__ y,
+    const int2* __restrict__ tiles, int mt_ub, int ntn, int gn,
+    int per_xcd) {
+  // one LDS object per stage, so the compiler can tell the block being read
+  // from the blocks still being copied
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kV2Stage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kV2Stage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds2[kV2Stage];
+  __shared__ float sw[2][kGemmMaxK / 128];
+  const int bid = blockIdx.x;
+  const int wi = ORDER == 1 ? (bid & 7) * per_xcd + (bid >> 3) : bid;
+  const int ng = wi / (mt_ub * gn);
+  const int rem = wi - ng * mt_ub * gn;
+  const int mt = rem / gn;
+  const int nt = ng * gn + (rem - mt * gn);
+  if (mt >= mt_ub || nt >= ntn) return;
+  const int2 tile = tiles[mt];
+  const int e = tile.x;
+  if (e < 0) return;
+  const int r0 = tile.y;
+  int r_end = offsets[e + 1];
+  r_end = r_end > cap ? cap : r_end;
+  r_end = r_end < r0 + kV2TM ? r_end : r0 + kV2TM;
+  if (r_end <= r0) return;
+  const int KB = K / 128;
+  const int NB = N / 128;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int wm = wv & 1, wn = wv >> 1;
+
+  // weight scales of the tile's two 128-column blocks
+  for (int i = tid; i < 2 * KB; i += 512) {
+    const int h = i / KB, b = i - h * KB;
+    const int nb = nt * 2 + h < NB ? nt * 2 + h : NB - 1;
+    sw[h][b] = wscale[((size_t)e * NB + nb) * KB + b];
+  }
+
+  // this lane's DMA sources (block 0); block b adds b * 128 (b for scales)
+  const size_t lane_k = 32 * g4;
+  int ra = r0 + 16 * wv + c16;
+  ra = ra < r_end ? ra : r_end - 1;
+  const unsigned char* asrc = rows + (size_t)ra * K + lane_k;
+  const unsigned char* bsrc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    int n = nt * kV2TN + 16 * (2 * wv + q) + c16;
+    n = n < N ? n : N - 1;
+    bsrc[q] = w + ((size_t)e * N + n) * K + lane_k;
+  }
+  // row scales: every wave copies the 64 rows it multiplies (rows 64 wm ..
+  // +64) into its own slot
+  int srow = r0 + 64 * wm + lane;
+  srow = srow < r_end ? srow : r_end - 1;
+  const float* ssrc = rscale + (size_t)srow * KB;
+  const int scopy = wv * 64;
+
+  auto issue = [&](int b, unsigned char* base) {
+    const size_t o = (size_t)b * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(asrc + o + 16 * h, base + (wv * 2 + h) * 1024);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dma16(bsrc[q] + o + 16 * h, base + kV2A + ((2 * wv + q) * 2 + h) * 1024);
+    dma4(ssrc + b, (float*)(base + kV2A + kV2B) + scopy);
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // staging through registers: block b + 1 is loaded during block b - 1 and
+  // written to LDS at the start of block b
+  u32x4 ra_[2], rb_[2][2];
+  float rs_;
+  auto load_regs = [&](int b) {
+    const size_t o = (size_t)b * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ra_[h] = ld16(asrc + o + 16 * h);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) rb_[q][h] = ld16(bsrc[q] + o + 16 * h);
+    rs_ = ssrc[b];
+  };
+  auto store_regs = [&](unsigned char* base) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<u32x4*>(base + (wv * 2 + h) * 1024 + lane * 16) = ra_[h];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(base + kV2A + ((2 * wv + q) * 2 + h) * 1024 +
+                                  lane * 16) = rb_[q][h];
+    ((float*)(base + kV2A + kV2B))[scopy + lane] = rs_;
+  };
+
+  auto block = [&](int b, const unsigned char* base, unsigned char* next1,
+                   unsigned char* next2) {
+    if constexpr (VIA_REGS) {
+      lds_barrier();
+      if (b + 1 < KB) store_regs(next1);
+      if (b + 2 < KB) load_regs(b + 2);
+    } else {
+      if (b + 1 < KB) wait_vm<kV2DmaPerWave>();
+      else wait_vm<0>();
+      lds_barrier();
+      if (b + 2 < KB) issue(b + 2, next2);
+    }
+    const float* sa = (const float*)(base + kV2A + kV2B) + scopy;
+    const float swb = sw[wn >> 1][b];
+    i32x8 fa[4], fb[4];
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned char* pa = base + ((4 * wm + i) * 2) * 1024 + lane * 16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(pa);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + 1024);
+      fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const unsigned char* pb =
+          base + kV2A + ((4 * wn + i) * 2) * 1024 + lane * 16;
+      const u32x4 blo = *reinterpret_cast<const u32x4*>(pb);
+      const u32x4 bhi = *reinterpret_cast<const u32x4*>(pb + 1024);
+      fb[i] = i32x8{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w,
+                    (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+      s[i] = sa[16 * i + c16] * swb;
+    }
+    f32x4 p[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        p[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            fb[j], fa[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[i][j][q], s[i], acc[i][j][q]);
+  };
+  if constexpr (VIA_REGS) {
+    load_regs(0);
+    store_regs(lds0);
+    if (KB > 1) load_regs(1);
+  } else {
+    issue(0, lds0);
+    if (KB > 1) issue(1, lds1);
+  }
+  __syncthreads();   // sw (and block 0) visible
+  for (int b = 0; b < KB; b += 3) {
+    block(b, lds0, lds1, lds2);
+    if (b + 1 < KB) block(b + 1, lds1, lds2, lds0);
+    if (b + 2 < KB) block(b + 2, lds2, lds0, lds1);
+  }
+
+  // lane: row 64 wm + 16 i + c16, columns 64 wn + 16 j + 4 g4 .. + 3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + 64 * wm + 16 * i + c16;
+    if (r >= r_end) continue;
+    const bool live = row_src == nullptr || row_src[r] >= 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = nt * kV2TN + 64 * wn + 16 * j + 4 * g4;
+      if (n >= N) continue;
+      f32x4 v = acc[i][j];
+      if (!live) v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (YT == 1) {
+        const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(y + ((size_t)r * N + n) * 2) = pk;
+      } else {
+        *reinterpret_cast<f32x4*>(y + ((size_t)r * N + n) * 4) = v;
+      }
+    }
+  }
+}
+
 hipError_t launch_expert_gemm(const void* rows, const float* row_scales,
                               int K, size_t rows_capacity,
                               const int32_t* row_src, const int32_t* offsets,
@@ -220,8 +447,10 @@ hipError_t launch_expert_gemm(const void* rows, const float* row_scales,
                      E, cap, (int)mt_ub, tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int ntn = N / kGemmTile;
-  const int gn = ntn < 8 ? ntn : 8;
+  // all column tiles of a row tile are consecutive: the row tile's
+  // activations stay in cache while the expert's weight panels stream
+  const int ntn = (N + kV2TN - 1) / kV2TN;
+  const int gn = ntn;
   const long long total = (long long)((ntn + gn - 1) / gn) * mt_ub * gn;
   const long long grid = (total + 7) / 8 * 8;
   const int per_xcd = (int)(grid / 8);
@@ -229,13 +458,13 @@ hipError_t launch_expert_gemm(const void* rows, const float* row_scales,
   const unsigned char* wb = (const unsigned char*)w;
   unsigned char* yb = (unsigned char*)y;
   if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<1>), dim3((unsigned)grid),
-                       dim3(256), 0, s, rb, row_scales, K, cap, row_src,
+    hipLaunchKernelGGL((expert_gemm_fp8_v2_kernel<1, 0, 1>), dim3((unsigned)grid),
+                       dim3(512), 0, s, rb, row_scales, K, cap, row_src,
                        offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
                        gn, per_xcd);
   else
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<0>), dim3((unsigned)grid),
-                       dim3(256), 0, s, rb, row_scales, K, cap, row_src,
+    hipLaunchKernelGGL((expert_gemm_fp8_v2_kernel<0, 0, 1>), dim3((unsigned)grid),
+                       dim3(512), 0, s, rb, row_scales, K, cap, row_src,
                        offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
                        gn, per_xcd);
   return hipGetLastError();
