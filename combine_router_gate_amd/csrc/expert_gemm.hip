@@ -87,180 +87,37 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
         tiles[start[e] + j] = make_int2(e, off[e] + j * kGemmTile);
 }
 
-// Operand fragment of 16 rows x 128 bytes: lane l holds bytes
-// [32 * (l / 16), +32) of row l % 16.  Both operands use the same byte
-// assignment, so the instruction's sum covers the block's 128 products.
-__device__ __forceinline__ i32x8 frag_ld(const unsigned char* p) {
-  const u32x4 a = ld16(p), b = ld16(p + 16);
-  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w,
-               (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-}
-
-template <int YT>
-__global__ __launch_bounds__(256, 2) void expert_gemm_fp8_kernel(
-    const unsigned char* __restrict__ rows, const float* __restrict__ rscale,
-    int K, int cap, const int32_t* __restrict__ row_src,
-    const int32_t* __restrict__ offsets, const unsigned char* __restrict__ w,
-    const float* __restrict__ wscale, int N, unsigned char* __restrict__ y,
-    const int2* __restrict__ tiles, int mt_ub, int ntn, int gn,
-    int per_xcd) {
-  __shared__ float sa[kGemmMaxK];          // [block][row of the tile]
-  __shared__ float sw[kGemmMaxK / 128];    // [block]
-  const int bid = blockIdx.x;
-  const int wi = (bid & 7) * per_xcd + (bid >> 3);
-  const int ng = wi / (mt_ub * gn);
-  const int rem = wi - ng * mt_ub * gn;
-  const int mt = rem / gn;
-  const int nt = ng * gn + (rem - mt * gn);
-  if (mt >= mt_ub || nt >= ntn) return;
-  const int2 tile = tiles[mt];
-  const int e = tile.x;
-  if (e < 0) return;
-  const int r0 = tile.y;
-  int r_end = offsets[e + 1];
-  r_end = r_end > cap ? cap : r_end;
-  r_end = r_end < r0 + kGemmTile ? r_end : r0 + kGemmTile;
-  if (r_end <= r0) return;
-  const int KB = K / 128;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int c16 = lane & 15, g = lane >> 4;
-  const int m0 = 64 * (wv & 1), n0 = 64 * (wv >> 1);
-
-  for (int i = tid; i < kGemmTile * KB; i += 256) {
-    const int row = i / KB, b = i - row * KB;
-    const int r = r0 + row < r_end ? r0 + row : r_end - 1;
-    sa[b * kGemmTile + row] = rscale[(size_t)r * KB + b];
-  }
-  const float* swp = wscale + ((size_t)e * (N / 128) + nt) * KB;
-  for (int b = tid; b < KB; b += 256) sw[b] = swp[b];
-  __syncthreads();
-
-  const unsigned char* ap[4];
-  const unsigned char* bp[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = r0 + m0 + 16 * i + c16;
-    r = r < r_end ? r : r_end - 1;
-    ap[i] = rows + (size_t)r * K + 32 * g;
-    const int n = nt * kGemmTile + n0 + 16 * i + c16;
-    bp[i] = w + ((size_t)e * N + n) * K + 32 * g;
-  }
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  auto load = [&](i32x8 (&fa)[4], i32x8 (&fb)[4], int b) {
-    const size_t o = (size_t)b * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = frag_ld(ap[i] + o);
-      fb[i] = frag_ld(bp[i] + o);
-    }
-  };
-  auto step = [&](const i32x8 (&fa)[4], const i32x8 (&fb)[4], int b) {
-    const float swb = sw[b];
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = sa[b * kGemmTile + m0 + 16 * i + c16] * swb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            fb[j], fa[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[q], s[i], acc[i][j][q]);
-      }
-  };
-  load(fa0, fb0, 0);
-  for (int b = 0; b < KB; b += 2) {
-    // blocks b (buffer 0) and b + 1 (buffer 1); loads stay one block ahead
-    // and are clamped to the last block so they are never conditional
-    load(fa1, fb1, b + 1 < KB ? b + 1 : KB - 1);
-    step(fa0, fb0, b);
-    load(fa0, fb0, b + 2 < KB ? b + 2 : KB - 1);
-    if (b + 1 < KB) step(fa1, fb1, b + 1);
-  }
-
-  // lane: row m0 + 16 i + c16, columns n0 + 16 j + 4 g .. + 3
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + m0 + 16 * i + c16;
-    if (r >= r_end) continue;
-    const bool live = row_src == nullptr || row_src[r] >= 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t n = (size_t)nt * kGemmTile + n0 + 16 * j + 4 * g;
-      f32x4 v = acc[i][j];
-      if (!live) v = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (YT == 1) {
-        const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(y + ((size_t)r * N + n) * 2) = pk;
-      } else {
-        *reinterpret_cast<f32x4*>(y + ((size_t)r * N + n) * 4) = v;
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ v2
-
-// Direct global -> LDS copy of 16 (or 4) bytes per lane; lane i's data lands
-// at lds + i * bytes (gfx950 global_load_lds_dwordx4 / _dword).
-__device__ __forceinline__ void dma16(const unsigned char* g, unsigned char* l) {
-  __builtin_amdgcn_global_load_lds(
-      (const void __attribute__((address_space(1)))*)g,
-      (void __attribute__((address_space(3)))*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const float* g, float* l) {
-  __builtin_amdgcn_global_load_lds(
-      (const void __attribute__((address_space(1)))*)g,
-      (void __attribute__((address_space(3)))*)l, 4, 0, 0);
-}
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // A workgroup computes a 128 (rows) x 256 (columns) tile with 8 waves (two
 // per SIMD); wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64,
-// i.e. 4 x 4 MFMA tiles.  Per 128-wide block each wave copies, straight into
-// LDS, one row group of the activation tile, two of the weight tile (16 rows
-// x 128 bytes each, in MFMA fragment order so every ds_read_b128 is
-// conflict-free) and 64 row scales; three blocks are in flight.  A block's 16
-// MFMAs are issued back to back into separate result registers, then their
-// results are scaled into the fp32 accumulators, so one wave's scaling runs
-// while the other wave's MFMAs occupy the matrix core.
-constexpr int kV2TM = 128, kV2TN = 256, kV2Stages = 3;
-constexpr int kV2A = kV2TM * 128, kV2B = kV2TN * 128;
-constexpr int kV2Scales = 8 * 64 * 4;                    // 64 rows per wave
-constexpr int kV2Stage = kV2A + kV2B + kV2Scales;
-constexpr int kV2DmaPerWave = 1 * 2 + 2 * 2 + 1;
+// i.e. 4 x 4 MFMA tiles.  Per 128-wide block each wave loads one row group
+// of the activation tile, two of the weight tile (16 rows x 128 bytes each)
+// and 64 row scales into registers two blocks ahead and writes them to LDS
+// one block ahead, in MFMA fragment order so every ds_read_b128 is
+// conflict-free.  Per activation fragment, 4 MFMAs are issued back to back
+// into separate result registers and then scaled into the fp32
+// accumulators, so one wave's scaling runs while the other wave's MFMAs
+// occupy the matrix core.
+constexpr int kTM = 128, kTN = 256;
+constexpr int kTileA = kTM * 128, kTileB = kTN * 128;
+constexpr int kTileS = 8 * 64 * 4;                    // 64 rows per wave
+constexpr int kStageBytes = kTileA + kTileB + kTileS;
 
-template <int YT, int ORDER, int VIA_REGS>
-__global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
+template <int YT>
+__global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     const unsigned char* __restrict__ rows, const float* __restrict__ rscale,
     int K, int cap, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ offsets, const unsigned char* __restrict__ w,
     const float* __restrict__ wscale, int N, unsigned char* __restrict__ y,
-    const int2* __restrict__ tiles, int mt_ub, int ntn, int gn,
-    int per_xcd) {
+    const int2* __restrict__ tiles, int mt_ub, int ntn, int gn) {
   // one LDS object per stage, so the compiler can tell the block being read
   // from the blocks still being copied
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kV2Stage];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kV2Stage];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds2[kV2Stage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds2[kStageBytes];
   __shared__ float sw[2][kGemmMaxK / 128];
   const int bid = blockIdx.x;
-  const int wi = ORDER == 1 ? (bid & 7) * per_xcd + (bid >> 3) : bid;
-  const int ng = wi / (mt_ub * gn);
-  const int rem = wi - ng * mt_ub * gn;
+  const int ng = bid / (mt_ub * gn);
+  const int rem = bid - ng * mt_ub * gn;
   const int mt = rem / gn;
   const int nt = ng * gn + (rem - mt * gn);
   if (mt >= mt_ub || nt >= ntn) return;
@@ -270,7 +127,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
   const int r0 = tile.y;
   int r_end = offsets[e + 1];
   r_end = r_end > cap ? cap : r_end;
-  r_end = r_end < r0 + kV2TM ? r_end : r0 + kV2TM;
+  r_end = r_end < r0 + kTM ? r_end : r0 + kTM;
   if (r_end <= r0) return;
   const int KB = K / 128;
   const int NB = N / 128;
@@ -286,7 +143,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
     sw[h][b] = wscale[((size_t)e * NB + nb) * KB + b];
   }
 
-  // this lane's DMA sources (block 0); block b adds b * 128 (b for scales)
+  // this lane's global sources (block 0); block b adds b * 128 (b for scales)
   const size_t lane_k = 32 * g4;
   int ra = r0 + 16 * wv + c16;
   ra = ra < r_end ? ra : r_end - 1;
@@ -294,7 +151,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
   const unsigned char* bsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    int n = nt * kV2TN + 16 * (2 * wv + q) + c16;
+    int n = nt * kTN + 16 * (2 * wv + q) + c16;
     n = n < N ? n : N - 1;
     bsrc[q] = w + ((size_t)e * N + n) * K + lane_k;
   }
@@ -304,19 +161,6 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
   srow = srow < r_end ? srow : r_end - 1;
   const float* ssrc = rscale + (size_t)srow * KB;
   const int scopy = wv * 64;
-
-  auto issue = [&](int b, unsigned char* base) {
-    const size_t o = (size_t)b * 128;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      dma16(asrc + o + 16 * h, base + (wv * 2 + h) * 1024);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        dma16(bsrc[q] + o + 16 * h, base + kV2A + ((2 * wv + q) * 2 + h) * 1024);
-    dma4(ssrc + b, (float*)(base + kV2A + kV2B) + scopy);
-  };
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -346,24 +190,19 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(base + kV2A + ((2 * wv + q) * 2 + h) * 1024 +
+        *reinterpret_cast<u32x4*>(base + kTileA + ((2 * wv + q) * 2 + h) * 1024 +
                                   lane * 16) = rb_[q][h];
-    ((float*)(base + kV2A + kV2B))[scopy + lane] = rs_;
+    ((float*)(base + kTileA + kTileB))[scopy + lane] = rs_;
   };
 
-  auto block = [&](int b, const unsigned char* base, unsigned char* next1,
-                   unsigned char* next2) {
-    if constexpr (VIA_REGS) {
-      lds_barrier();
-      if (b + 1 < KB) store_regs(next1);
-      if (b + 2 < KB) load_regs(b + 2);
-    } else {
-      if (b + 1 < KB) wait_vm<kV2DmaPerWave>();
-      else wait_vm<0>();
-      lds_barrier();
-      if (b + 2 < KB) issue(b + 2, next2);
-    }
-    const float* sa = (const float*)(base + kV2A + kV2B) + scopy;
+  auto block = [&](int b, const unsigned char* base, unsigned char* next1) {
+    __builtin_amdgcn_sched_barrier(0);   // keep blocks apart
+    // unconditional (clamped) copies keep the compiler's wait counts
+    // exact; past the last block they are redundant and never read
+    lds_barrier();
+    store_regs(next1);
+    load_regs(b + 2 < KB ? b + 2 : KB - 1);
+    const float* sa = (const float*)(base + kTileA + kTileB) + scopy;
     const float swb = sw[wn >> 1][b];
     i32x8 fa[4], fb[4];
     float s[4];
@@ -375,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
       fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       const unsigned char* pb =
-          base + kV2A + ((4 * wn + i) * 2) * 1024 + lane * 16;
+          base + kTileA + ((4 * wn + i) * 2) * 1024 + lane * 16;
       const u32x4 blo = *reinterpret_cast<const u32x4*>(pb);
       const u32x4 bhi = *reinterpret_cast<const u32x4*>(pb + 1024);
       fb[i] = i32x8{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w,
@@ -397,20 +236,20 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[i][j][q], s[i], acc[i][j][q]);
   };
-  if constexpr (VIA_REGS) {
-    load_regs(0);
-    store_regs(lds0);
-    if (KB > 1) load_regs(1);
-  } else {
-    issue(0, lds0);
-    if (KB > 1) issue(1, lds1);
-  }
+  load_regs(0);
+  store_regs(lds0);
+  load_regs(KB > 1 ? 1 : 0);
   __syncthreads();   // sw (and block 0) visible
-  for (int b = 0; b < KB; b += 3) {
-    block(b, lds0, lds1, lds2);
-    if (b + 1 < KB) block(b + 1, lds1, lds2, lds0);
-    if (b + 2 < KB) block(b + 2, lds2, lds0, lds1);
+  // block b reads stage b % 3; three blocks per iteration with no branch
+  // between them (exact wait counts), then the remaining blocks
+  int b = 0;
+  for (; b + 3 <= KB; b += 3) {
+    block(b, lds0, lds1);
+    block(b + 1, lds1, lds2);
+    block(b + 2, lds2, lds0);
   }
+  if (b < KB) block(b, lds0, lds1);
+  if (b + 1 < KB) block(b + 1, lds1, lds2);
 
   // lane: row 64 wm + 16 i + c16, columns 64 wn + 16 j + 4 g4 .. + 3
 #pragma unroll
@@ -420,7 +259,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_v2_kernel(
     const bool live = row_src == nullptr || row_src[r] >= 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = nt * kV2TN + 64 * wn + 16 * j + 4 * g4;
+      const int n = nt * kTN + 64 * wn + 16 * j + 4 * g4;
       if (n >= N) continue;
       f32x4 v = acc[i][j];
       if (!live) v = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -449,24 +288,23 @@ hipError_t launch_expert_gemm(const void* rows, const float* row_scales,
   if (err != hipSuccess) return err;
   // all column tiles of a row tile are consecutive: the row tile's
   // activations stay in cache while the expert's weight panels stream
-  const int ntn = (N + kV2TN - 1) / kV2TN;
+  const int ntn = (N + kTN - 1) / kTN;
   const int gn = ntn;
   const long long total = (long long)((ntn + gn - 1) / gn) * mt_ub * gn;
-  const long long grid = (total + 7) / 8 * 8;
-  const int per_xcd = (int)(grid / 8);
+  const long long grid = total;
   const unsigned char* rb = (const unsigned char*)rows;
   const unsigned char* wb = (const unsigned char*)w;
   unsigned char* yb = (unsigned char*)y;
   if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((expert_gemm_fp8_v2_kernel<1, 0, 1>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<1>), dim3((unsigned)grid),
                        dim3(512), 0, s, rb, row_scales, K, cap, row_src,
                        offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
-                       gn, per_xcd);
+                       gn);
   else
-    hipLaunchKernelGGL((expert_gemm_fp8_v2_kernel<0, 0, 1>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<0>), dim3((unsigned)grid),
                        dim3(512), 0, s, rb, row_scales, K, cap, row_src,
                        offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
-                       gn, per_xcd);
+                       gn);
   return hipGetLastError();
 }
 
