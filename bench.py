@@ -27,8 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 # Kernel sources whose hash keys the committed counter-based traffic figure
 COMBINE_SOURCES = ["combine_router_gate_amd/csrc/combine.hip",
-                   "combine_router_gate_amd/csrc/moe_device.h",
-                   "combine_router_gate_amd/csrc/moe_launch.h"]
+                   "combine_router_gate_amd/csrc/moe_device.h"]
 TRAFFIC_PROFILE = "profiles/traffic_combine_kernel_dsv3_prefill.txt"
 
 
