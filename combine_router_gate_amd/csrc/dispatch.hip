@@ -122,49 +122,60 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
       }
     }
   } else {
-    // 16 consecutive elements per lane; 8 lanes per 128-element block
+    // 16 consecutive elements per lane; 8 lanes per 128-element block; two
+    // 64-lane chunks per iteration, both loaded before either is used, with
+    // loads clamped to the row (never conditional) so they stay in flight
+    // together
+    constexpr int EB = MODE == 1 ? 32 : 64;    // source bytes per lane chunk
+    constexpr int U = 2;
     const int nc16 = H / 16;
     const int nblk = H / kFp8Block;
     const unsigned char* src = x + (size_t)t * H * esize;
-    for (int c0 = part * 64; c0 < nc16; c0 += hsplit * 64) {
-      const int c = c0 + lane;
-      const bool ok = c < nc16;
-      float f[16];
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      if constexpr (MODE == 1) {
-        const unsigned char* p = src + (size_t)c * 32;
-        unpack8_bf16(ok ? ld16_stream(p) : z, f);
-        unpack8_bf16(ok ? ld16_stream(p + 16) : z, f + 8);
-      } else {
-        const unsigned char* p = src + (size_t)c * 64;
+    for (int c0 = part * 64 * U; c0 < nc16; c0 += hsplit * 64 * U) {
+      u32x4 v[U][EB / 16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v = ok ? ld16_stream(p + 16 * q) : z;
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64 + lane;
+        const unsigned char* p = src + (size_t)(c < nc16 ? c : nc16 - 1) * EB;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) f[4 * q + i] = __uint_as_float(v[i]);
-        }
+        for (int q = 0; q < EB / 16; ++q) v[u][q] = ld16_stream(p + 16 * q);
       }
-      float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64 + lane;
+        float f[16];
+        if constexpr (MODE == 1) {
+          unpack8_bf16(v[u][0], f);
+          unpack8_bf16(v[u][1], f + 8);
+        } else {
 #pragma unroll
-      for (int m = 4; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 8));
-      // scale and quotient are IEEE fp32 operations (correctly rounded)
-      const float s = amax > 0.0f ? amax / kFp8Max : 1.0f;
-      float q[16];
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = f[i] / s;
-      u32x4 pk;
-      pk.x = e4m3_encode4(q[0], q[1], q[2], q[3]);
-      pk.y = e4m3_encode4(q[4], q[5], q[6], q[7]);
-      pk.z = e4m3_encode4(q[8], q[9], q[10], q[11]);
-      pk.w = e4m3_encode4(q[12], q[13], q[14], q[15]);
-      if (ok) {
+            for (int i = 0; i < 4; ++i) f[4 * q + i] = __uint_as_float(v[u][q][i]);
+        }
+        float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-          if (rj[j] < 0) continue;
-          st16_stream(rows + (size_t)rj[j] * H + (size_t)c * 16, pk);
-          if ((lane & 7) == 0) row_scales[(size_t)rj[j] * nblk + c / 8] = s;
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+        for (int m = 4; m >= 1; m >>= 1)
+          amax = fmaxf(amax, __shfl_xor(amax, m, 8));
+        // scale and quotient are IEEE fp32 operations (correctly rounded)
+        const float s = amax > 0.0f ? amax / kFp8Max : 1.0f;
+        float q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = f[i] / s;
+        u32x4 pk;
+        pk.x = e4m3_encode4(q[0], q[1], q[2], q[3]);
+        pk.y = e4m3_encode4(q[4], q[5], q[6], q[7]);
+        pk.z = e4m3_encode4(q[8], q[9], q[10], q[11]);
+        pk.w = e4m3_encode4(q[12], q[13], q[14], q[15]);
+        if (c < nc16) {
+#pragma unroll
+          for (int j = 0; j < KMAX; ++j) {
+            if (rj[j] < 0) continue;
+            st16_stream(rows + (size_t)rj[j] * H + (size_t)c * 16, pk);
+            if ((lane & 7) == 0) row_scales[(size_t)rj[j] * nblk + c / 8] = s;
+          }
         }
       }
     }
@@ -281,7 +292,7 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
   const int mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
   // waves per token: about 2048 waves in flight for few tokens, at most one
   // per group of 64-lane chunks of the row
-  const int groups = mode == 0 ? (H * esize / 16 + 127) / 128 : (H / 16 + 63) / 64;
+  const int groups = mode == 0 ? (H * esize / 16 + 127) / 128 : (H / 16 + 127) / 128;
   int hs = (2048 + T - 1) / (T > 0 ? T : 1);
   hs = hs < groups ? hs : groups;
   hs = hs < 1 ? 1 : hs;

@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 // the same pipeline as gate_topk_v2_kernel over [k_lo, k_lo + KR) and
 // writes its fp32 partial logits partial[ks][t][e] (row stride 64*EPW).
 // gate_reduce_topk_kernel adds the ranges in ascending order.
-template <int EPW, int TT, int PQ, int D>
+template <int EPW, int TT, int PQ, int D, int DX = D>
 __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
     int H, int E, int KR, float* __restrict__ partial,
@@ -500,7 +500,10 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     wrow[et] = w + (size_t)(e < E ? e : E - 1) * H;
   }
 
-  u32x4 xreg[D][XPT];
+  // x streams from HBM (DX steps in flight), the gate weight from L2 (D)
+  constexpr int L = DX > D ? DX : D;
+  static_assert(L % D == 0 && L % DX == 0, "prefetch depths must nest");
+  u32x4 xreg[DX][XPT];
   u32x4 wreg[D][EPW][PQ];
   auto load_x = [&](int i, u32x4 (&dst)[XPT]) {
 #pragma unroll
@@ -526,23 +529,23 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     for (int et = 0; et < EPW; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    load_x(j, xreg[j]);
-    load_w(j, wreg[j]);
-  }
-  for (int i0 = 0; i0 < nss; i0 += D) {
+  for (int j = 0; j < DX; ++j) load_x(j, xreg[j]);
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int i = i0 + j;
+  for (int j = 0; j < D; ++j) load_w(j, wreg[j]);
+  for (int i0 = 0; i0 < nss; i0 += L) {
+#pragma unroll
+    for (int jj = 0; jj < L; ++jj) {
+      const int i = i0 + jj;
+      const int jx = jj % DX, j = jj % D;
       unsigned char* slot = lds + (i & 1) * XSLOT;
 #pragma unroll
       for (int m = 0; m < XPT; ++m) {
         const bool ok = xrow_ok[m] && k_lo + i * KS + xp[m] * 8 < k_hi;
         st16(slot + xr[m] * RB + ((xp[m] ^ (xr[m] & (NP - 1))) * 16),
-             ok ? xreg[j][m] : z);
+             ok ? xreg[jx][m] : z);
       }
       lds_barrier();
-      load_x(i + D, xreg[j]);
+      load_x(i + DX, xreg[jx]);
 #pragma unroll
       for (int q = 0; q < PQ; ++q) {
 #pragma unroll
@@ -1068,6 +1071,9 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
 #define MOE_GATE_PART(EPWV, TTV, DV)                                           \
   hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV>), pgrid,          \
                      dim3(256), 0, s, x, w, T, H, E, KR, part, done)
+#define MOE_GATE_PART_X(EPWV, TTV, DV, DXV)                                    \
+  hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV, DXV>), pgrid,     \
+                     dim3(256), 0, s, x, w, T, H, E, KR, part, done)
 #define MOE_GATE_PART_E(TTV)                                                   \
   do {                                                                         \
     if (epw == 1) MOE_GATE_PART(1, TTV, 4);                                    \
@@ -1079,13 +1085,14 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       if (TT == 8) {
         if (epw == 1) MOE_GATE_PART(1, 8, 3);
         else if (epw == 2) MOE_GATE_PART(2, 8, 3);
-        else MOE_GATE_PART(4, 8, 2);
+        else MOE_GATE_PART_X(4, 8, 2, 4);   // x 4 steps ahead: +5%
       } else if (TT == 4) {
         MOE_GATE_PART_E(4);
       } else {
         MOE_GATE_PART_E(2);
       }
 #undef MOE_GATE_PART_E
+#undef MOE_GATE_PART_X
 #undef MOE_GATE_PART
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
