@@ -8,12 +8,13 @@
 
 namespace moe {
 
-constexpr int kGemmTile = 128;      // output tile rows and columns
-constexpr int kGemmMaxK = 8192;     // row scales of a tile are staged in LDS
+constexpr int kGemmRowsPerTile = 256;   // output rows per workgroup tile
+constexpr int kGemmMaxK = 8192;
 
-// Upper bound on the 128-row tiles of all expert segments.
+// Upper bound on the 128-row tiles of all expert segments (also bounds the
+// number of tiles of any larger row count).
 inline long long gemm_row_tiles(size_t rows_capacity, int E) {
-  return (long long)((rows_capacity + kGemmTile - 1) / kGemmTile) + E;
+  return (long long)((rows_capacity + 127) / 128) + E;
 }
 inline size_t gemm_workspace_bytes(size_t rows_capacity, int E) {
   return ((size_t)gemm_row_tiles(rows_capacity, E) * 8 + 255) & ~size_t(255);

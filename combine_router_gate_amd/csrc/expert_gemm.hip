@@ -21,10 +21,12 @@
 //  * The weight tile is the instruction's first operand, so each lane ends
 //    up with 4 consecutive output columns of one row: one row scale per
 //    lane and block, 8-byte bf16 stores.
-//  * A workgroup computes a 128x256 tile with 8 waves (two per SIMD, 64x64
-//    each); operands are staged through LDS in MFMA fragment order
-//    (conflict-free 16-byte reads), three blocks deep, loaded through
-//    registers (direct global->LDS copies measured slower on this part).
+//  * A workgroup computes a 256x256 tile with 8 waves (two per SIMD, 128x64
+//    each); operands are staged through two LDS stages in MFMA fragment
+//    order (conflict-free 16-byte reads), loaded through registers (direct
+//    global->LDS copies measured slower on this part).  256-row tiles move a
+//    third fewer bytes per flop than 128-row ones; a tile whose second half
+//    lies past its segment skips that half.
 //  * Work order: all column tiles of one row tile are consecutive, so the
 //    row tile's activations stay cached while the expert's weights stream.
 //  * Row tiles come from a tile map built on the device from offsets, so no
@@ -37,11 +39,11 @@ namespace moe {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// tiles[mt] = (expert, first row) for every 128-row tile of the padded
+// tiles[mt] = (expert, first row) for every tm-row tile of the padded
 // expert segments, (-1, 0) for the unused entries up to mt_ub.  Offsets are
 // clamped to the buffer so a corrupt plan cannot address past it.
 __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
-    const int32_t* __restrict__ offsets, int E, int cap, int mt_ub,
+    const int32_t* __restrict__ offsets, int E, int cap, int mt_ub, int tm,
     int2* __restrict__ tiles) {
   __shared__ int off[MOE_MAX_EXPERTS + 1];
   __shared__ int start[MOE_MAX_EXPERTS + 1];
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
     for (int i = 0; i < PER; ++i) {
       const int e = tid * PER + i;
       const int seg = e < E ? off[e + 1] - off[e] : 0;
-      loc[i] = seg > 0 ? (seg + kGemmTile - 1) / kGemmTile : 0;
+      loc[i] = seg > 0 ? (seg + tm - 1) / tm : 0;
       sum += loc[i];
     }
     int incl = sum;
@@ -84,36 +86,42 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
   for (int e = tid; e < E; e += 512)
     for (int j = 0; start[e] + j < start[e + 1]; ++j)
       if (start[e] + j < mt_ub)
-        tiles[start[e] + j] = make_int2(e, off[e] + j * kGemmTile);
+        tiles[start[e] + j] = make_int2(e, off[e] + j * tm);
 }
 
-// A workgroup computes a 128 (rows) x 256 (columns) tile with 8 waves (two
-// per SIMD); wave (wm, wn) owns rows 64 wm .. +64 and columns 64 wn .. +64,
-// i.e. 4 x 4 MFMA tiles.  Per 128-wide block each wave loads one row group
-// of the activation tile, two of the weight tile (16 rows x 128 bytes each)
-// and 64 row scales into registers two blocks ahead and writes them to LDS
-// one block ahead, in MFMA fragment order so every ds_read_b128 is
-// conflict-free.  Per activation fragment, 4 MFMAs are issued back to back
-// into separate result registers and then scaled into the fp32
-// accumulators, so one wave's scaling runs while the other wave's MFMAs
-// occupy the matrix core.
-constexpr int kTM = 128, kTN = 256;
-constexpr int kTileA = kTM * 128, kTileB = kTN * 128;
-constexpr int kTileS = 8 * 64 * 4;                    // 64 rows per wave
-constexpr int kStageBytes = kTileA + kTileB + kTileS;
+// A workgroup computes a TMR (rows, 128 or 256) x 256 (columns) tile with 8
+// waves (two per SIMD); wave (wm, wn) owns rows TMR/2 wm .. +TMR/2 and
+// columns 64 wn .. +64, i.e. TMR/32 x 4 MFMA tiles.  Per 128-wide block each
+// wave loads TMR/128 row groups of the activation tile, two of the weight
+// tile (16 rows x 128 bytes each) and its rows' scales into registers two
+// blocks ahead and writes them to LDS one block ahead, in MFMA fragment
+// order so every ds_read_b128 is conflict-free (two LDS stages).  Per
+// activation fragment, 4 MFMAs are issued back to back into separate result
+// registers and then scaled into the fp32 accumulators, so one wave's
+// scaling runs while the other wave's MFMAs occupy the matrix core.  A tile
+// whose second row half lies past its segment skips that half's copies and
+// MFMAs.
+constexpr int kTN = 256;
+template <int TMR> struct GemmTile {
+  static constexpr int A = TMR * 128, B = kTN * 128;
+  static constexpr int S = 8 * (TMR / 2) * 4;       // each wave's rows' scales
+  static constexpr int Stage = A + B + S;
+  static constexpr int MI = TMR / 32;               // row fragments per wave
+  static constexpr int AG = TMR / 128;              // row groups copied per wave
+};
 
-template <int YT>
+template <int YT, int TMR>
 __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     const unsigned char* __restrict__ rows, const float* __restrict__ rscale,
     int K, int cap, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ offsets, const unsigned char* __restrict__ w,
     const float* __restrict__ wscale, int N, unsigned char* __restrict__ y,
     const int2* __restrict__ tiles, int mt_ub, int ntn, int gn) {
+  using G = GemmTile<TMR>;
   // one LDS object per stage, so the compiler can tell the block being read
-  // from the blocks still being copied
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds2[kStageBytes];
+  // from the block being written
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::Stage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::Stage];
   __shared__ float sw[2][kGemmMaxK / 128];
   const int bid = blockIdx.x;
   const int ng = bid / (mt_ub * gn);
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   const int r0 = tile.y;
   int r_end = offsets[e + 1];
   r_end = r_end > cap ? cap : r_end;
-  r_end = r_end < r0 + kTM ? r_end : r0 + kTM;
+  r_end = r_end < r0 + TMR ? r_end : r0 + TMR;
   if (r_end <= r0) return;
   const int KB = K / 128;
   const int NB = N / 128;
@@ -135,6 +143,8 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   const int lane = tid & 63, wv = tid >> 6;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int wm = wv & 1, wn = wv >> 1;
+  // this wave's row half holds rows of the segment (uniform per wave)
+  const bool half_live = (TMR / 2) * wm < r_end - r0;
 
   // weight scales of the tile's two 128-column blocks
   for (int i = tid; i < 2 * KB; i += 512) {
@@ -145,9 +155,16 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
 
   // this lane's global sources (block 0); block b adds b * 128 (b for scales)
   const size_t lane_k = 32 * g4;
-  int ra = r0 + 16 * wv + c16;
-  ra = ra < r_end ? ra : r_end - 1;
-  const unsigned char* asrc = rows + (size_t)ra * K + lane_k;
+  const unsigned char* asrc[G::AG];
+  bool aload[G::AG];
+#pragma unroll
+  for (int q = 0; q < G::AG; ++q) {
+    const int grp = G::AG * wv + q;
+    aload[q] = 16 * grp < r_end - r0;          // row group holds segment rows
+    int r = r0 + 16 * grp + c16;
+    r = r < r_end ? r : r_end - 1;
+    asrc[q] = rows + (size_t)r * K + lane_k;
+  }
   const unsigned char* bsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -155,44 +172,59 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     n = n < N ? n : N - 1;
     bsrc[q] = w + ((size_t)e * N + n) * K + lane_k;
   }
-  // row scales: every wave copies the 64 rows it multiplies (rows 64 wm ..
-  // +64) into its own slot
-  int srow = r0 + 64 * wm + lane;
-  srow = srow < r_end ? srow : r_end - 1;
-  const float* ssrc = rscale + (size_t)srow * KB;
-  const int scopy = wv * 64;
-
-  f32x4 acc[4][4];
+  // row scales: every wave copies the rows it multiplies into its own slot
+  const float* ssrc[G::AG];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int q = 0; q < G::AG; ++q) {
+    int srow = r0 + (TMR / 2) * wm + 64 * q + lane;
+    srow = srow < r_end ? srow : r_end - 1;
+    ssrc[q] = rscale + (size_t)srow * KB;
+  }
+  const int scopy = wv * (TMR / 2);
+
+  f32x4 acc[G::MI][4];
+#pragma unroll
+  for (int i = 0; i < G::MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // staging through registers: block b + 1 is loaded during block b - 1 and
   // written to LDS at the start of block b
-  u32x4 ra_[2], rb_[2][2];
-  float rs_;
+  u32x4 ra_[G::AG][2], rb_[2][2];
+  float rs_[G::AG];
   auto load_regs = [&](int b) {
     const size_t o = (size_t)b * 128;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ra_[h] = ld16(asrc + o + 16 * h);
+    for (int q = 0; q < G::AG; ++q)
+      if (aload[q]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ra_[q][h] = ld16(asrc[q] + o + 16 * h);
+      }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h) rb_[q][h] = ld16(bsrc[q] + o + 16 * h);
-    rs_ = ssrc[b];
+#pragma unroll
+    for (int q = 0; q < G::AG; ++q) rs_[q] = ssrc[q][b];
   };
   auto store_regs = [&](unsigned char* base) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<u32x4*>(base + (wv * 2 + h) * 1024 + lane * 16) = ra_[h];
+    for (int q = 0; q < G::AG; ++q)
+      if (aload[q]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<u32x4*>(base + ((G::AG * wv + q) * 2 + h) * 1024 +
+                                    lane * 16) = ra_[q][h];
+      }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(base + kTileA + ((2 * wv + q) * 2 + h) * 1024 +
+        *reinterpret_cast<u32x4*>(base + G::A + ((2 * wv + q) * 2 + h) * 1024 +
                                   lane * 16) = rb_[q][h];
-    ((float*)(base + kTileA + kTileB))[scopy + lane] = rs_;
+#pragma unroll
+    for (int q = 0; q < G::AG; ++q)
+      ((float*)(base + G::A + G::B))[scopy + 64 * q + lane] = rs_[q];
   };
 
   auto block = [&](int b, const unsigned char* base, unsigned char* next1) {
@@ -202,59 +234,57 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     lds_barrier();
     store_regs(next1);
     load_regs(b + 2 < KB ? b + 2 : KB - 1);
-    const float* sa = (const float*)(base + kTileA + kTileB) + scopy;
+    if (!half_live) return;
+    const float* sa = (const float*)(base + G::A + G::B) + scopy;
     const float swb = sw[wn >> 1][b];
-    i32x8 fa[4], fb[4];
-    float s[4];
+    i32x8 fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned char* pa = base + ((4 * wm + i) * 2) * 1024 + lane * 16;
+    for (int j = 0; j < 4; ++j) {
+      const unsigned char* pb =
+          base + G::A + ((4 * wn + j) * 2) * 1024 + lane * 16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(pb);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + 1024);
+      fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int i = 0; i < G::MI; ++i) {
+      const unsigned char* pa =
+          base + ((G::MI * wm + i) * 2) * 1024 + lane * 16;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(pa);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + 1024);
-      fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const unsigned char* pb =
-          base + kTileA + ((4 * wn + i) * 2) * 1024 + lane * 16;
-      const u32x4 blo = *reinterpret_cast<const u32x4*>(pb);
-      const u32x4 bhi = *reinterpret_cast<const u32x4*>(pb + 1024);
-      fb[i] = i32x8{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w,
-                    (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
-      s[i] = sa[16 * i + c16] * swb;
+      const i32x8 fa = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const float si = sa[16 * i + c16] * swb;
+      f32x4 p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[j][q], si, acc[i][j][q]);
     }
-    f32x4 p[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        p[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            fb[j], fa[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[i][j][q], s[i], acc[i][j][q]);
   };
   load_regs(0);
   store_regs(lds0);
   load_regs(KB > 1 ? 1 : 0);
   __syncthreads();   // sw (and block 0) visible
-  // block b reads stage b % 3; three blocks per iteration with no branch
-  // between them (exact wait counts), then the remaining blocks
+  // block b reads stage b % 2; two blocks per iteration with no branch
+  // between them (exact wait counts), then the last one
   int b = 0;
-  for (; b + 3 <= KB; b += 3) {
+  for (; b + 2 <= KB; b += 2) {
     block(b, lds0, lds1);
-    block(b + 1, lds1, lds2);
-    block(b + 2, lds2, lds0);
+    block(b + 1, lds1, lds0);
   }
   if (b < KB) block(b, lds0, lds1);
-  if (b + 1 < KB) block(b + 1, lds1, lds2);
 
-  // lane: row 64 wm + 16 i + c16, columns 64 wn + 16 j + 4 g4 .. + 3
+  // lane: row TMR/2 wm + 16 i + c16, columns 64 wn + 16 j + 4 g4 .. + 3
+  if (!half_live) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + 64 * wm + 16 * i + c16;
+  for (int i = 0; i < G::MI; ++i) {
+    const int r = r0 + (TMR / 2) * wm + 16 * i + c16;
     if (r >= r_end) continue;
     const bool live = row_src == nullptr || row_src[r] >= 0;
 #pragma unroll
@@ -279,29 +309,29 @@ hipError_t launch_expert_gemm(const void* rows, const float* row_scales,
                               int E, const void* w, const float* w_scales,
                               int N, void* y, int y_dtype, void* workspace,
                               hipStream_t s) {
+  constexpr int TMR = kGemmRowsPerTile;
   const long long mt_ub = gemm_row_tiles(rows_capacity, E);
   int2* tiles = (int2*)workspace;
   const int cap = (int)rows_capacity;
   hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(512), 0, s, offsets,
-                     E, cap, (int)mt_ub, tiles);
+                     E, cap, (int)mt_ub, TMR, tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // all column tiles of a row tile are consecutive: the row tile's
   // activations stay in cache while the expert's weight panels stream
   const int ntn = (N + kTN - 1) / kTN;
   const int gn = ntn;
-  const long long total = (long long)((ntn + gn - 1) / gn) * mt_ub * gn;
-  const long long grid = total;
+  const long long grid = mt_ub * gn;
   const unsigned char* rb = (const unsigned char*)rows;
   const unsigned char* wb = (const unsigned char*)w;
   unsigned char* yb = (unsigned char*)y;
   if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<1>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<1, TMR>), dim3((unsigned)grid),
                        dim3(512), 0, s, rb, row_scales, K, cap, row_src,
                        offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
                        gn);
   else
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<0>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((expert_gemm_fp8_kernel<0, TMR>), dim3((unsigned)grid),
                        dim3(512), 0, s, rb, row_scales, K, cap, row_src,
                        offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
                        gn);

@@ -32,6 +32,9 @@ CASES = {
                                                 pad=8), 128, "f32"),
     "e64_k8_k1024": (C["dsv3_decode"].with_shape(T=128, H=1024, E=64,
                                                  payload="fp8"), 512, "bf16"),
+    # segments of ~300 rows: several row tiles per expert, a half-empty last
+    "e4_long_segments": (C["dsv3_prefill"].with_shape(T=600, H=256, E=4, k=2,
+                                                      pad=128), 384, "f32"),
 }
 
 
