@@ -8,7 +8,7 @@
 
 namespace moe {
 
-constexpr int kGemmRowsPerTile = 256;   // output rows per workgroup tile
+constexpr int kGemmRowsPerTile = 128;   // output rows per workgroup tile
 constexpr int kGemmMaxK = 8192;
 
 // Upper bound on the 128-row tiles of all expert segments (also bounds the

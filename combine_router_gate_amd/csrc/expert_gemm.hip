@@ -21,12 +21,15 @@
 //  * The weight tile is the instruction's first operand, so each lane ends
 //    up with 4 consecutive output columns of one row: one row scale per
 //    lane and block, 8-byte bf16 stores.
-//  * A workgroup computes a 256x256 tile with 8 waves (two per SIMD, 128x64
-//    each); operands are staged through two LDS stages in MFMA fragment
-//    order (conflict-free 16-byte reads), loaded through registers (direct
-//    global->LDS copies measured slower on this part).  256-row tiles move a
-//    third fewer bytes per flop than 128-row ones; a tile whose second half
-//    lies past its segment skips that half.
+//  * A workgroup computes a 128x256 tile with 8 waves (two per SIMD, 64x64
+//    each; 256-row tiles need more registers than a wave has and spill);
+//    operands are staged through two LDS stages in MFMA fragment order,
+//    loaded through registers (direct global->LDS copies measured slower on
+//    this part).  Global loads are coalesced (8 lanes per 128-byte row
+//    segment) and scattered into fragment order in LDS with an XOR swizzle
+//    that keeps writes and fragment reads free of bank conflicts: with one
+//    row per lane the address unit handled every 16-byte access separately
+//    and was 72% busy.
 //  * Work order: all column tiles of one row tile are consecutive, so the
 //    row tile's activations stay cached while the expert's weights stream.
 //  * Row tiles come from a tile map built on the device from offsets, so no
@@ -153,25 +156,45 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     sw[h][b] = wscale[((size_t)e * NB + nb) * KB + b];
   }
 
-  // this lane's global sources (block 0); block b adds b * 128 (b for scales)
-  const size_t lane_k = 32 * g4;
-  const unsigned char* asrc[G::AG];
+  // Copies are coalesced: a 16-row x 128-byte group is two loads of 8 rows,
+  // 8 lanes per row reading its 128 bytes (piece p = lane & 7).  Each piece
+  // is written to its place in MFMA fragment order: piece p of row r16 is
+  // half p & 1 of the fragment of lane r16 + 16 (p >> 1).  Fragment slots
+  // are XOR-swizzled within their 16-slot bank row so that both these
+  // writes and the fragment reads are free of LDS bank conflicts.
+  auto slot_ofs = [](int h, int m, int c) {          // byte offset in a group
+    return h * 1024 + (16 * m + (c ^ (4 * m) ^ (2 * h))) * 16;
+  };
+  const int lp = lane & 7, lr = lane >> 3;
+  int wofs[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) wofs[u] = slot_ofs(lp & 1, lp >> 1, 8 * u + lr);
+  const int rofs0 = slot_ofs(0, g4, c16), rofs1 = slot_ofs(1, g4, c16);
+  // this lane's sources (block 0) as 32-bit byte offsets from uniform
+  // bases (cap * K and N * K fit in 32 bits); block b adds b * 128
+  const unsigned char* wexp = w + (size_t)e * N * K;
+  uint32_t aoff[G::AG][2];
   bool aload[G::AG];
 #pragma unroll
   for (int q = 0; q < G::AG; ++q) {
     const int grp = G::AG * wv + q;
     aload[q] = 16 * grp < r_end - r0;          // row group holds segment rows
-    int r = r0 + 16 * grp + c16;
-    r = r < r_end ? r : r_end - 1;
-    asrc[q] = rows + (size_t)r * K + lane_k;
-  }
-  const unsigned char* bsrc[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    int n = nt * kTN + 16 * (2 * wv + q) + c16;
-    n = n < N ? n : N - 1;
-    bsrc[q] = w + ((size_t)e * N + n) * K + lane_k;
+    for (int u = 0; u < 2; ++u) {
+      int r = r0 + 16 * grp + 8 * u + lr;
+      r = r < r_end ? r : r_end - 1;
+      aoff[q][u] = (uint32_t)r * (uint32_t)K + 16 * lp;
+    }
   }
+  uint32_t boff[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int n = nt * kTN + 16 * (2 * wv + q) + 8 * u + lr;
+      n = n < N ? n : N - 1;
+      boff[q][u] = (uint32_t)n * (uint32_t)K + 16 * lp;
+    }
   // row scales: every wave copies the rows it multiplies into its own slot
   const float* ssrc[G::AG];
 #pragma unroll
@@ -198,12 +221,12 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     for (int q = 0; q < G::AG; ++q)
       if (aload[q]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) ra_[q][h] = ld16(asrc[q] + o + 16 * h);
+        for (int u = 0; u < 2; ++u) ra_[q][u] = ld16(rows + aoff[q][u] + o);
       }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) rb_[q][h] = ld16(bsrc[q] + o + 16 * h);
+      for (int u = 0; u < 2; ++u) rb_[q][u] = ld16(wexp + boff[q][u] + o);
 #pragma unroll
     for (int q = 0; q < G::AG; ++q) rs_[q] = ssrc[q][b];
   };
@@ -212,16 +235,16 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     for (int q = 0; q < G::AG; ++q)
       if (aload[q]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<u32x4*>(base + ((G::AG * wv + q) * 2 + h) * 1024 +
-                                    lane * 16) = ra_[q][h];
+        for (int u = 0; u < 2; ++u)
+          *reinterpret_cast<u32x4*>(base + (G::AG * wv + q) * 2048 + wofs[u]) =
+              ra_[q][u];
       }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(base + G::A + ((2 * wv + q) * 2 + h) * 1024 +
-                                  lane * 16) = rb_[q][h];
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<u32x4*>(base + G::A + (2 * wv + q) * 2048 +
+                                  wofs[u]) = rb_[q][u];
 #pragma unroll
     for (int q = 0; q < G::AG; ++q)
       ((float*)(base + G::A + G::B))[scopy + 64 * q + lane] = rs_[q];
@@ -240,19 +263,17 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     i32x8 fb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const unsigned char* pb =
-          base + G::A + ((4 * wn + j) * 2) * 1024 + lane * 16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(pb);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + 1024);
+      const unsigned char* pb = base + G::A + (4 * wn + j) * 2048;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + rofs0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + rofs1);
       fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int i = 0; i < G::MI; ++i) {
-      const unsigned char* pa =
-          base + ((G::MI * wm + i) * 2) * 1024 + lane * 16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(pa);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + 1024);
+      const unsigned char* pa = base + (G::MI * wm + i) * 2048;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + rofs0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + rofs1);
       const i32x8 fa = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       const float si = sa[16 * i + c16] * swb;

@@ -338,7 +338,8 @@ int moe_expert_gemm_fp8(const void* rows, const float* row_scales, int K,
                         void* stream) {
   if (K < 128 || K % 128 != 0 || K > moe::kGemmMaxK || N < 128 ||
       N % 128 != 0 || E < 1 || E > MOE_MAX_EXPERTS ||
-      rows_capacity > (size_t)0x7fffffff)
+      rows_capacity * (size_t)K > (size_t)0xffffffff ||
+      (size_t)N * (size_t)K > (size_t)0xffffffff)
     return MOE_ERR_SHAPE;
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (rows_capacity == 0) return MOE_OK;

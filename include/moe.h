@@ -299,7 +299,8 @@ int moe_dispatch_backward(const void* grad_rows, int rows_dtype, int H,
  *   y          [rows_capacity, N] y_dtype (MOE_BF16 or MOE_F32); rows outside
  *              every segment are not written
  *   workspace  >= moe_expert_gemm_workspace_bytes(rows_capacity, E) bytes
- * K and N multiples of 128, K <= 8192.  Segment bounds are clamped to
+ * K and N multiples of 128, K <= 8192, rows_capacity * K and N * K below
+ * 2^32 (MOE_ERR_SHAPE otherwise).  Segment bounds are clamped to
  * rows_capacity.
  */
 size_t moe_expert_gemm_workspace_bytes(size_t rows_capacity, int E);
