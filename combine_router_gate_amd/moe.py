@@ -6,9 +6,13 @@ current HIP stream.  There is no fallback: if the library is not built this
 module raises on first use.
 
 Low-level functions carry the C names (``moe_route``, ``moe_plan``,
-``moe_dispatch``, ``moe_combine_residual``, ``moe_expert_fixture``) and take
-preallocated tensors; ``route`` / ``dispatch`` / ``combine_residual`` /
-``expert_fixture`` allocate their outputs with torch and call them.
+``moe_dispatch``, ``moe_combine_residual``, ``moe_farskip_aux``,
+``moe_combine_backward``, ``moe_dispatch_backward``, ``moe_expert_gemm_fp8``,
+``moe_expert_fixture``) and take preallocated tensors; ``route`` / ``plan`` /
+``dispatch`` / ``combine_residual`` / ``farskip_aux`` /
+``combine_main_residual`` / ``combine_backward`` / ``dispatch_backward`` /
+``expert_gemm_fp8`` / ``expert_fixture`` allocate their outputs with torch
+and call them.
 """
 from __future__ import annotations
 
