@@ -940,74 +940,130 @@ __global__ __launch_bounds__(512) void plan_small_kernel(
                   slot_rank, bits, ecnt);
 }
 
-// Reduction of the split gate for few tokens.  A workgroup of RW waves
-// covers 4 tokens (16 lanes each); wave w adds the ranges w, w + RW, ... in
-// ascending order, then wave 0 adds the RW wave sums in wave order (fixed
-// order: the logits do not depend on timing) and selects the top-k.  Each
-// workgroup then publishes its results (device-scope fence) and counts
-// itself done; the last one builds the plan of all tokens.  The counter is
+// Maximum over the 64 lanes of a wave (result uniform): 16-lane DPP maxima,
+// then the four row maxima read into scalar registers.
+__device__ __forceinline__ unsigned long long max64_u64(unsigned long long v) {
+  v = max16_u64(v);
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 16 * r);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 16 * r);
+    const unsigned long long x = ((unsigned long long)hi << 32) | lo;
+    m = x > m ? x : m;
+  }
+  return m;
+}
+
+// Reduction of the split gate for few tokens: a workgroup of 8 waves covers
+// TPW tokens with WPT = 8 / TPW waves each.  Wave p of a token adds the
+// ranges p, p + WPT, ... in ascending order, each lane holding C4 groups of
+// 4 consecutive experts (16-byte loads across the whole logit row); the
+// token's first wave adds its WPT wave sums in wave order (fixed order: the
+// logits do not depend on timing) and selects the top-k with all 64 lanes
+// (same 64-bit keys and tie-break as topk_select_write).  Each workgroup
+// then publishes its results (device-scope release) and counts itself done;
+// the last one acquires and builds the plan of all tokens.  The counter is
 // zeroed by gate_partial_kernel, which precedes this kernel on the stream.
-template <int ET, int RW>
-__global__ __launch_bounds__(64 * RW) void gate_reduce_plan_small_kernel(
+template <int C4, int TPW>
+__global__ __launch_bounds__(512) void gate_reduce_plan_small_kernel(
     const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
     int pad, const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits_dbg,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank,
     unsigned* __restrict__ done) {
-  constexpr int NT = 64 * RW;
-  constexpr int B = ET <= 16 ? 4 : 2;           // ranges in flight per wave
-  constexpr int RED = RW * 4 * 16 * ET;         // floats of wave sums
+  constexpr int RW = 8, NT = 64 * RW, B = 8;    // waves, threads, ranges in flight
+  constexpr int WPT = RW / TPW;                 // waves per token
+  constexpr int RED = RW * 64 * C4 * 4;         // floats of wave sums
   constexpr int BITS = (kSmallPlanT / 64) * MOE_MAX_EXPERTS;
   constexpr int LDS64 = RED / 2 > BITS ? RED / 2 : BITS;
   __shared__ unsigned long long lds[LDS64];
   __shared__ int ecnt[MOE_MAX_EXPERTS];
   __shared__ int last;
-  float* red = (float*)lds;
+  f32x4* red = (f32x4*)lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int t = blockIdx.x * 4 + g;
-  const int tc = t < T ? t : T - 1;
+  const int tk = wv / WPT, part = wv - tk * WPT;
+  const int t = blockIdx.x * TPW + tk;
+  const bool live = t < T;
+  const int tc = live ? t : T - 1;
+  const int nc4 = EPS / 4;                      // 16-byte groups of a row
 
-  float v[ET];
+  f32x4 v[C4];
 #pragma unroll
-  for (int et = 0; et < ET; ++et) v[et] = 0.0f;
-  for (int q0 = wv; q0 < S; q0 += B * RW) {
-    float u[B][ET];
+  for (int c = 0; c < C4; ++c) v[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q0 = part; q0 < S; q0 += B * WPT) {
+    f32x4 u[B][C4];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int q = q0 + b * RW < S ? q0 + b * RW : q0;
-      const float* pq = partial + ((size_t)q * T + tc) * EPS;
+      const int q = q0 + b * WPT < S ? q0 + b * WPT : q0;
+      const f32x4* pq = (const f32x4*)(partial + ((size_t)q * T + tc) * EPS);
 #pragma unroll
-      for (int et = 0; et < ET; ++et) {
-        const int e = et * 16 + c16;
-        u[b][et] = pq[e < E ? e : 0];
+      for (int c = 0; c < C4; ++c) {
+        const int ci = lane + 64 * c;
+        u[b][c] = pq[ci < nc4 ? ci : 0];
       }
     }
 #pragma unroll
     for (int b = 0; b < B; ++b)
-      if (q0 + b * RW < S) {
+      if (q0 + b * WPT < S) {
 #pragma unroll
-        for (int et = 0; et < ET; ++et) v[et] += u[b][et];
+        for (int c = 0; c < C4; ++c) v[c] += u[b][c];
       }
   }
 #pragma unroll
-  for (int et = 0; et < ET; ++et)
-    red[((wv * 4 + g) * ET + et) * 16 + c16] = v[et];
+  for (int c = 0; c < C4; ++c) red[(wv * C4 + c) * 64 + lane] = v[c];
   __syncthreads();
-  if (wv == 0) {
+  if (part == 0 && live) {
+    unsigned long long key[C4 * 4];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      float a = red[(g * ET + et) * 16 + c16];
-      for (int w = 1; w < RW; ++w) a += red[((w * 4 + g) * ET + et) * 16 + c16];
-      const int e = et * 16 + c16;
-      a += (bias != nullptr && e < E) ? bias[e] : 0.0f;
-      if (logits_dbg != nullptr && t < T && e < E)
-        logits_dbg[(size_t)t * E + e] = a;
-      v[et] = a;
+    for (int c = 0; c < C4; ++c) {
+      f32x4 a = red[(wv * C4 + c) * 64 + lane];
+      for (int w = 1; w < WPT; ++w) a += red[((wv + w) * C4 + c) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (lane + 64 * c) + i;
+        const bool ok = e < E && lane + 64 * c < nc4;
+        const float l = a[i] + ((bias != nullptr && ok) ? bias[e] : 0.0f);
+        if (logits_dbg != nullptr && ok) logits_dbg[(size_t)t * E + e] = l;
+        key[c * 4 + i] = ok ? ((unsigned long long)f32_order_key(l) << 32) |
+                                  (0xffffffffu - (uint32_t)e)
+                            : 0ull;
+      }
     }
-    topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w);
+    int sel_e[MOE_MAX_TOPK];
+    float sel_v[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      sel_e[j] = 0;
+      sel_v[j] = 0.0f;
+      if (j < k) {
+        unsigned long long best = key[0];
+#pragma unroll
+        for (int i = 1; i < C4 * 4; ++i) best = key[i] > best ? key[i] : best;
+        best = max64_u64(best);
+        const uint32_t blo = (uint32_t)best;
+#pragma unroll
+        for (int i = 0; i < C4 * 4; ++i)
+          if ((uint32_t)key[i] == blo) key[i] &= 0xffffffffull;
+        sel_e[j] = (int)(0xffffffffu - blo);
+        sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
+      }
+    }
+    float ex[MOE_MAX_TOPK];
+    float den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      ex[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.0f;
+      den += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k && lane == j) {
+        topk_idx[(size_t)t * k + j] = sel_e[j];
+        topk_w[(size_t)t * k + j] = ex[j] / den;
+      }
   }
   // release this workgroup's top-k, count it done; the last one acquires
   // every other workgroup's results before planning
@@ -1100,17 +1156,17 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       if (small) {
         // one kernel: reduction, top-k, and in its last workgroup the
         // histogram, scan and ranks of all tokens
+        // 4 tokens per workgroup keeps the completion count (one atomic per
+        // workgroup on one counter) at T / 4
         const dim3 rgrid((T + 3) / 4);
-#define MOE_GATE_SMALL(ETV)                                                    \
-  hipLaunchKernelGGL((gate_reduce_plan_small_kernel<ETV, 8>), rgrid,          \
-                     dim3(512), 0, s, part, S, EPS, T, E, k, pad, bias, idx,  \
-                     tw, dbg, counts, offsets, tb, sr, done)
-        if (epw == 1) MOE_GATE_SMALL(4);
-        else if (epw == 2) MOE_GATE_SMALL(8);
-        else if (epw == 4) MOE_GATE_SMALL(16);
-        else if (epw == 6) MOE_GATE_SMALL(24);
-        else MOE_GATE_SMALL(32);
-#undef MOE_GATE_SMALL
+        if (epw <= 4)
+          hipLaunchKernelGGL((gate_reduce_plan_small_kernel<1, 4>), rgrid,
+                             dim3(512), 0, s, part, S, EPS, T, E, k, pad, bias,
+                             idx, tw, dbg, counts, offsets, tb, sr, done);
+        else
+          hipLaunchKernelGGL((gate_reduce_plan_small_kernel<2, 4>), rgrid,
+                             dim3(512), 0, s, part, S, EPS, T, E, k, pad, bias,
+                             idx, tw, dbg, counts, offsets, tb, sr, done);
         *stage = kRouteDone;
         return hipGetLastError();
       }
