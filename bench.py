@@ -8,10 +8,13 @@ already resident in HBM.  The stand-in expert between dispatch and combine is
 not part of the transform: its output is produced once before timing (the
 dispatched rows, and hence the expert output, are identical every step).
 
-Prints one JSON line.  value = achieved HBM GB/s of dispatch + combine
-(algorithmic bytes / their measured time), the headline metric; the line
-also carries per-stage times, the roofline of the dominant kernel
-(combine) and the CPU-oracle baseline.
+Prints one JSON line.  ms_per_step: K steps launched back to back between
+two events.  value = achieved HBM GB/s of dispatch + combine (algorithmic
+bytes / their time, from K further steps with an event between stages), the
+headline metric; the line also carries per-stage times, the roofline of the
+dominant kernel (combine), the CPU-oracle baseline and, unless --no-extras,
+the fp8 expert GEMM, the backward passes, the FarSkip split/overlap and a
+HIP-graph replay of the layer.
 """
 import argparse
 import json
@@ -268,6 +271,37 @@ def measure_expert_gemm(cfg, moe, d, p, dev, iters=5):
     }
 
 
+def measure_graph(layer, stream, iters=20):
+    """One layer (route + dispatch + combine) captured once into a HIP graph
+    and replayed: µs per replay, against the same launches issued eagerly.
+    The path issues no memset and allocates nothing, so it captures as is."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        layer()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+    return {"graph_us_per_layer": round(timed(g.replay), 2),
+            "eager_us_per_layer": round(timed(layer), 2), "replays": iters}
+
+
 def measure_farskip_overlap(cfg, moe, y, tok_row, topk_w, shared, resid,
                             stream, dev, iters=10, n_next=2112):
     """FarSkip split form on one GPU: the auxiliary residual stream first
@@ -430,18 +464,25 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-           for _ in range(args.steps)]
+    # timed region: K steps launched back to back
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # stage breakdown: K more steps with an event between stages (events
+    # between launches add a little time to the smallest workloads, so they
+    # stay out of the timed region above)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     r_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     d_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     c_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -498,6 +539,17 @@ def main():
                                  for q in (10, 50, 90)]
     if args.cold_cache:
         line["cold_cache"] = measure_cold(step, stream, dev)
+    if not args.no_extras:
+        def layer():   # the timed step's launches, on the current stream
+            moe.moe_route(x, w, bias, k, pad, p["topk_idx"], p["topk_w"],
+                          p["counts"], p["offsets"], None, p["workspace"])
+            moe.moe_dispatch(x, p["topk_idx"], E, pad, p["counts"],
+                             p["offsets"], p["workspace"], d["payload_dtype"],
+                             d["rows"], d["row_scales"], d["row_src"],
+                             d["tok_row"])
+            moe.moe_combine_residual(y, d["tok_row"], p["topk_w"], shared,
+                                     resid, res_out, rnr, out)
+        line["hip_graph"] = measure_graph(layer, stream)
     if not args.no_extras and cfg.payload == "fp8":
         line["expert_gemm"] = measure_expert_gemm(cfg, moe, d, p, dev)
     if not args.no_extras:
