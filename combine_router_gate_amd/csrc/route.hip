@@ -579,6 +579,149 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     }
 }
 
+// The same partial logits for many tokens (the same MFMAs in the same order
+// per accumulator, so the same bits), with both operands staged through LDS
+// by coalesced loads: 8 lanes fetch one 128-byte row segment, so a
+// gate-weight segment is read once per workgroup and 64-wide k block rather
+// than once per lane group and fragment.  x is loaded three blocks ahead of
+// its use into two register sets (from HBM), the gate weight two blocks
+// ahead into one (from L2); block b is computed from one LDS stage while
+// block b+1 is written into the other.  The 2-block loop has no branches
+// and its loads are unconditional (clamped to the range), which keeps the
+// compiler's wait counts exact instead of draining every load each
+// iteration.  Rows are XOR-swizzled in LDS by gate_lds_swz so that both the
+// coalesced 16-byte writes and the fragment reads hit distinct banks.
+// Requires every range to be whole 128-element pairs of blocks
+// (H % 128 == 0, KR % 128 == 0) and byte offsets below 2^32.
+__device__ __forceinline__ int gate_lds_swz(int r) {
+  return (r & 7) ^ ((r >> 3) & 1);
+}
+
+template <int EPW, int TT>
+__global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
+    int H, int E, int KR, float* __restrict__ partial,
+    unsigned* __restrict__ done) {
+  if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 &&
+      threadIdx.x == 0)
+    *done = 0u;
+  // 8 waves: wave wv owns tokens 16 TT (wv >> 2) + [0, 16 TT) and experts
+  // 16 EPW (wv & 3) + [0, 16 EPW) of the workgroup's tile
+  constexpr int EP = 64 * EPW;             // padded experts
+  constexpr int TTOK = 32 * TT;            // tokens of the workgroup
+  constexpr int XS = TTOK * 128;           // bytes of x in one stage
+  constexpr int STG = XS + EP * 128;       // bytes of one stage
+  constexpr int XPT = TTOK / 64;           // x pieces per thread and block
+  constexpr int WPT = EP / 64;             // weight pieces per thread, block
+  __shared__ __align__(16) unsigned char lds[2 * STG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * TTOK;
+  const int k_lo = blockIdx.y * KR;
+  const int nb = (min(H, k_lo + KR) - k_lo) / 64;   // even, >= 2
+
+  // this thread loads rows (tid >> 3) + 64 m, 16-byte piece tid & 7
+  const int pr = tid >> 3, pc = tid & 7;
+  const unsigned char* xb =
+      reinterpret_cast<const unsigned char*>(x) + (size_t)k_lo * 2 + pc * 16;
+  const unsigned char* wb =
+      reinterpret_cast<const unsigned char*>(w) + (size_t)k_lo * 2 + pc * 16;
+  const uint32_t rowb = (uint32_t)H * 2u;
+  uint32_t xo[XPT], wo[WPT];
+#pragma unroll
+  for (int m = 0; m < XPT; ++m)
+    xo[m] = (uint32_t)min(t0 + pr + 64 * m, T - 1) * rowb;
+#pragma unroll
+  for (int m = 0; m < WPT; ++m)
+    wo[m] = (uint32_t)min(pr + 64 * m, E - 1) * rowb;
+  // LDS byte offset of this thread's pieces (row pr + 64 m has pr's swizzle)
+  const int dsto = pr * 128 + ((pc ^ gate_lds_swz(pr)) * 16);
+  // fragment reads: row 16 j + c16 of the wave's rows, piece 2 g + q
+  const int sw = gate_lds_swz(c16);
+  const int frx = ((wv >> 2) * 16 * TT + c16) * 128;
+  const int frw = XS + ((wv & 3) * 16 * EPW + c16) * 128;
+
+  u32x4 xs[2][XPT], ws[WPT];
+  auto load_x = [&](int b, u32x4 (&dst)[XPT]) {
+    const uint32_t kb = (uint32_t)min(b, nb - 1) * 128u;
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) dst[m] = ld16_stream(xb + xo[m] + kb);
+  };
+  auto load_w = [&](int b) {
+    const uint32_t kb = (uint32_t)min(b, nb - 1) * 128u;
+#pragma unroll
+    for (int m = 0; m < WPT; ++m) ws[m] = ld16(wb + wo[m] + kb);
+  };
+  auto store = [&](unsigned char* stage, const u32x4 (&src)[XPT]) {
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) st16(stage + dsto + m * 64 * 128, src[m]);
+#pragma unroll
+    for (int m = 0; m < WPT; ++m)
+      st16(stage + XS + dsto + m * 64 * 128, ws[m]);
+  };
+
+  f32x4 acc[TT][EPW];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const unsigned char* stage, int q) {
+    const int po = ((2 * g + q) ^ sw) * 16;
+    Frag<uint16_t> b[EPW], a[TT];
+#pragma unroll
+    for (int et = 0; et < EPW; ++et)
+      b[et].v = *reinterpret_cast<const u32x4*>(stage + frw + et * 16 * 128 + po);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+      a[tt].v = *reinterpret_cast<const u32x4*>(stage + frx + tt * 16 * 128 + po);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int et = 0; et < EPW; ++et)
+        acc[tt][et] = mfma_step(a[tt], b[et], acc[tt][et]);
+  };
+
+  // block b computes stage b & 1, writes block b+1 (its weight loaded at
+  // b-1, its x at b-2) into the other stage, then loads the weight of b+2
+  // and the x of b+3 into the set it just stored
+  load_w(0);
+  load_x(0, xs[0]);
+  load_x(1, xs[1]);
+  store(lds, xs[0]);
+  load_w(1);
+  load_x(2, xs[0]);
+  lds_barrier();
+  for (int b = 0; b < nb; b += 2) {
+    compute(lds, 0);
+    store(lds + STG, xs[1]);
+    load_w(b + 2);
+    load_x(b + 3, xs[1]);
+    compute(lds, 1);
+    lds_barrier();
+    compute(lds + STG, 0);
+    store(lds, xs[0]);
+    load_w(b + 3);
+    load_x(b + 4, xs[0]);
+    compute(lds + STG, 1);
+    lds_barrier();
+  }
+  float* out = partial + (size_t)blockIdx.y * T * EP;
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) {
+      const int e = ((wv & 3) * EPW + et) * 16 + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + (wv >> 2) * 16 * TT + tt * 16 + g * 4 + i;
+        if (t < T) out[(size_t)t * EP + e] = acc[tt][et][i];
+      }
+    }
+}
+
 // Sum of the S partial logits (ranges in ascending order) + bias, then the
 // top-k of every token.  A workgroup of WAVES waves covers
 // 4 * WAVES * PASSES tokens (4 per wave and pass); when that is one 64-token
@@ -1105,17 +1248,26 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   if constexpr (sizeof(XT) == 2) {
     const int epw = gate_epw(E);
     // Split the hidden dimension so the partial GEMM runs about 256
-    // workgroups (128 for few tokens, whose reduction is the bottleneck).
-    // With 128-token tiles every gate-weight fragment a wave loads feeds 8
-    // MFMAs, which halves each CU's gate-weight traffic per token; that and
-    // a full chip beat the fused single pass even at 16K tokens.
-    const int TT = (epw <= 4 && T >= 8192) ? 8 : T >= 2048 ? 4 : 2;
+    // workgroups (128 for few tokens, whose reduction is the bottleneck);
+    // with a full chip that beats the fused single pass even at 16K tokens.
+    // From 4096 tokens the LDS-staged kernel takes 128-token tiles with
+    // coalesced loads of both operands; it needs hidden ranges of whole
+    // 128-element block pairs and 32-bit byte offsets.  Otherwise
+    // gate_partial_kernel, whose lane groups load gate-weight fragments
+    // directly (128-token tiles at 8K tokens and up halve that traffic).
+    const bool lds_gate = T >= 4096 && H % 128 == 0 &&
+                          (epw <= 4 || epw == 6) &&
+                          (size_t)T * H * 2 <= 0xffffffffu &&
+                          (size_t)E * H * 2 <= 0xffffffffu;
+    const int TT = lds_gate ? 8
+                   : (epw <= 4 && T >= 8192) ? 8 : T >= 2048 ? 4 : 2;
     const int tiles = (T + 16 * TT - 1) / (16 * TT);
     const int target = T >= 2048 ? 256 : 128;
+    const int kq = lds_gate ? 128 : 64;    // range granularity
     int S = (target + tiles - 1) / tiles;
-    S = min(S, min(split_max(T), (H + 63) / 64));
+    S = min(S, min(split_max(T), (H + kq - 1) / kq));
     if (S > 1) {
-      const int KR = ((H + S - 1) / S + 63) / 64 * 64;
+      const int KR = ((H + S - 1) / S + kq - 1) / kq * kq;
       S = (H + KR - 1) / KR;
       float* part = (float*)((unsigned char*)sr + ws_rank_bytes(T, k));
       const bool small = T <= kSmallPlanT;
@@ -1138,7 +1290,15 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     else if (epw == 6) MOE_GATE_PART(6, TTV, 3);                               \
     else MOE_GATE_PART(8, TTV, 2);                                             \
   } while (0)
-      if (TT == 8) {
+#define MOE_GATE_LDS(EPWV)                                                     \
+  hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, 4>), pgrid, dim3(512), 0, \
+                     s, x, w, T, H, E, KR, part, done)
+      if (lds_gate) {
+        if (epw == 1) MOE_GATE_LDS(1);
+        else if (epw == 2) MOE_GATE_LDS(2);
+        else if (epw == 4) MOE_GATE_LDS(4);
+        else MOE_GATE_LDS(6);
+      } else if (TT == 8) {
         if (epw == 1) MOE_GATE_PART(1, 8, 3);
         else if (epw == 2) MOE_GATE_PART(2, 8, 3);
         else MOE_GATE_PART_X(4, 8, 2, 4);   // x 4 steps ahead: +5%
@@ -1147,6 +1307,7 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       } else {
         MOE_GATE_PART_E(2);
       }
+#undef MOE_GATE_LDS
 #undef MOE_GATE_PART_E
 #undef MOE_GATE_PART_X
 #undef MOE_GATE_PART

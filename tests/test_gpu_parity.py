@@ -50,6 +50,14 @@ SMALL = {
                                               zipf_bias=False),
     "small_t512": C["dsv3_decode"].with_shape(T=512, H=1024, k=6, pad=16),
     "small_t1": C["dsv3_decode"].with_shape(T=1, H=2048),
+    # many tokens: the LDS-staged partial gate (2 and 1 expert tiles per
+    # wave, ragged token tile, 128-wide hidden ranges) and its fallback for
+    # H not a multiple of 128
+    "lds_gate_t4100_e100": C["dsv3_prefill"].with_shape(T=4100, H=512, E=100,
+                                                        k=6, pad=32),
+    "lds_gate_t4096_e64": C["mixtral"].with_shape(T=4096, H=384, E=64, k=4,
+                                                  pad=16),
+    "gate_t4096_h1032": C["dsv3_decode"].with_shape(T=4096, H=1032, E=256),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 
@@ -103,6 +111,8 @@ INT_CASES = {
     "int_f32_e20": C["tiny"].with_shape(T=99, H=64, E=20, k=3, pad=2),
     "int_e384_fp8": C["moonep_skew"].with_shape(T=130, H=256, payload="fp8",
                                                zipf_bias=False),
+    # many tokens (LDS-staged partial gate)
+    "int_t4096_e256": C["dsv3_decode"].with_shape(T=4096, H=256, E=256, k=8),
 }
 
 
