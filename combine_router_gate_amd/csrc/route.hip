@@ -99,7 +99,15 @@ __device__ __forceinline__ f32x4 mfma_step(const Frag<float>& a,
 // by clearing its high word, which leaves it below every real key (the key
 // of any non-NaN logit has a non-zero high word).  Lane j of the group
 // writes the j-th choice and its renormalised weight.
-template <int ET>
+// Lane c of a 16-lane group holds expert 16 et + c in v[et], or with QUAD
+// expert 64 (et / 4) + 4 c + et % 4 (four consecutive experts per 16-byte
+// load).
+template <bool QUAD>
+__device__ __forceinline__ int topk_expert(int et, int c) {
+  return QUAD ? 64 * (et >> 2) + 4 * c + (et & 3) : et * 16 + c;
+}
+
+template <int ET, bool QUAD = false>
 __device__ __forceinline__ void topk_select_write(
     const float (&v)[ET], int t, int T, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -109,7 +117,7 @@ __device__ __forceinline__ void topk_select_write(
   unsigned long long key[ET];
 #pragma unroll
   for (int et = 0; et < ET; ++et) {
-    const int e = et * 16 + c;
+    const int e = topk_expert<QUAD>(et, c);
     const uint32_t hi = e < E ? f32_order_key(v[et]) : 0u;
     key[et] = ((unsigned long long)hi << 32) | (0xffffffffu - (uint32_t)e);
   }
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 // grid is (token tiles of 16*TT, hidden ranges of KR), each workgroup runs
 // the same pipeline as gate_topk_v2_kernel over [k_lo, k_lo + KR) and
 // writes its fp32 partial logits partial[ks][t][e] (row stride 64*EPW).
-// gate_reduce_topk_kernel adds the ranges in ascending order.
+// gate_reduce_quad_kernel adds the ranges in ascending order.
 template <int EPW, int TT, int PQ, int D, int DX = D>
 __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
@@ -600,11 +608,22 @@ __device__ __forceinline__ int gate_lds_swz(int r) {
 template <int EPW, int TT>
 __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, float* __restrict__ partial,
+    int H, int E, int KR, int tiles, int xg, float* __restrict__ partial,
     unsigned* __restrict__ done) {
-  if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 &&
-      threadIdx.x == 0)
-    *done = 0u;
+  if (done != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *done = 0u;
+  // One-dimensional grid of tiles * S workgroups; workgroup i runs on XCD
+  // i % 8.  With xg = 8 / S (S dividing 8, tiles a multiple of xg) every XCD
+  // serves one hidden range, so its L2 holds 1/S of the gate weight;
+  // otherwise tiles vary fastest.
+  int tile, ks;
+  if (xg > 0) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    tile = slot * xg + xcd % xg;
+    ks = xcd / xg;
+  } else {
+    tile = blockIdx.x % tiles;
+    ks = blockIdx.x / tiles;
+  }
   // 8 waves: wave wv owns tokens 16 TT (wv >> 2) + [0, 16 TT) and experts
   // 16 EPW (wv & 3) + [0, 16 EPW) of the workgroup's tile
   constexpr int EP = 64 * EPW;             // padded experts
@@ -618,8 +637,8 @@ __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int t0 = blockIdx.x * TTOK;
-  const int k_lo = blockIdx.y * KR;
+  const int t0 = tile * TTOK;
+  const int k_lo = ks * KR;
   const int nb = (min(H, k_lo + KR) - k_lo) / 64;   // even, >= 2
 
   // this thread loads rows (tid >> 3) + 64 m, 16-byte piece tid & 7
@@ -708,7 +727,7 @@ __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
     compute(lds + STG, 1);
     lds_barrier();
   }
-  float* out = partial + (size_t)blockIdx.y * T * EP;
+  float* out = partial + (size_t)ks * T * EP;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -722,100 +741,101 @@ __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
     }
 }
 
-// Sum of the S partial logits (ranges in ascending order) + bias, then the
-// top-k of every token.  A workgroup of WAVES waves covers
-// 4 * WAVES * PASSES tokens (4 per wave and pass); when that is one 64-token
-// tile it also writes the tile's histogram and slot ranks.
-template <int ET, int WAVES, int PASSES>
-__global__ __launch_bounds__(64 * WAVES) void gate_reduce_topk_kernel(
-    const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
+// Sum of the S partial logits (ranges in ascending order), then the bias,
+// and the top-k of every token, for 4 * WAVES tokens per workgroup (the
+// tile histogram and ranks when that is 64).  The 16 lanes of a group own one
+// token and lane c holds experts 64 j + 4 c + i (i < 4), so each 16-byte
+// load reads four consecutive logits and a group reads 256 contiguous
+// bytes; CH ranges are loaded together (clamped; the repeats are not
+// added), so for S <= CH every load of a token is in flight at once.
+template <int EPW, int WAVES, int CH>
+__global__ __launch_bounds__(64 * WAVES) void gate_reduce_quad_kernel(
+    const float* __restrict__ partial, int S, int T, int E, int k,
     const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits_dbg,
     int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank) {
-  constexpr int NT = 64 * WAVES;
-  constexpr int TOK = 4 * WAVES * PASSES;
+  constexpr int EP = 64 * EPW, ET = 4 * EPW;
+  constexpr int NT = 64 * WAVES, TOK = 4 * WAVES;
   constexpr bool HIST = TOK == 64;
-  __shared__ unsigned long long tile_bits[HIST ? 16 * ET : 1];
+  __shared__ unsigned long long tile_bits[HIST ? EP : 1];
   __shared__ int tile_sel[HIST ? 64 * MOE_MAX_TOPK : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int t0 = blockIdx.x * TOK;
+  const int tl = wv * 4 + g;
+  const int t = t0 + tl;
+  const int tc = t < T ? t : T - 1;
   if constexpr (HIST) {
-    for (int e = tid; e < 16 * ET; e += NT) tile_bits[e] = 0ull;
+    for (int e = tid; e < EP; e += NT) tile_bits[e] = 0ull;
     __syncthreads();
   }
-  float bv[ET];
+  const float* row = partial + (size_t)tc * EP + 4 * c16;
+  const size_t rs = (size_t)T * EP;        // stride between ranges
+  float v[ET];
+  auto load = [&](int q0, f32x4 (&u)[CH][EPW]) {
+#pragma unroll
+    for (int b = 0; b < CH; ++b) {
+      const int q = q0 + b < S ? q0 + b : S - 1;
+#pragma unroll
+      for (int j = 0; j < EPW; ++j)
+        u[b][j] = __builtin_bit_cast(f32x4, ld16(row + q * rs + 64 * j));
+    }
+  };
+  {
+    f32x4 u[CH][EPW];
+    load(0, u);
+#pragma unroll
+    for (int j = 0; j < EPW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * j + i] = u[0][j][i];
+#pragma unroll
+    for (int b = 1; b < CH; ++b)
+      if (b < S) {
+#pragma unroll
+        for (int j = 0; j < EPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * j + i] += u[b][j][i];
+      }
+  }
+  for (int q0 = CH; q0 < S; q0 += CH) {
+    f32x4 u[CH][EPW];
+    load(q0, u);
+#pragma unroll
+    for (int b = 0; b < CH; ++b)
+      if (q0 + b < S) {
+#pragma unroll
+        for (int j = 0; j < EPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * j + i] += u[b][j][i];
+      }
+  }
 #pragma unroll
   for (int et = 0; et < ET; ++et) {
-    const int e = et * 16 + c16;
-    bv[et] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+    const int e = topk_expert<true>(et, c16);
+    v[et] += (bias != nullptr && e < E) ? bias[e] : 0.0f;
+    if (logits_dbg != nullptr && t < T && e < E)
+      logits_dbg[(size_t)t * E + e] = v[et];
   }
-#pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    const int tl = (wv * PASSES + pass) * 4 + g;
-    const int t = t0 + tl;
-    const int tc = t < T ? t : T - 1;
-    // partial sums in ascending range order; loads batched four ranges at
-    // a time (clamped, unconditional) so they are in flight together
-    float v[ET];
-#pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      const int e = et * 16 + c16;
-      v[et] = partial[(size_t)tc * EPS + (e < E ? e : 0)];
-    }
-    for (int q0 = 1; q0 < S; q0 += 4) {
-      float u[4][ET];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int q = q0 + b < S ? q0 + b : S - 1;
-        const float* pq = partial + ((size_t)q * T + tc) * EPS;
-#pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          const int e = et * 16 + c16;
-          u[b][et] = pq[e < E ? e : 0];
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (q0 + b < S) {
-#pragma unroll
-          for (int et = 0; et < ET; ++et) v[et] += u[b][et];
-        }
-    }
-#pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      v[et] += bv[et];
-      const int e = et * 16 + c16;
-      if (logits_dbg != nullptr && t < T && e < E)
-        logits_dbg[(size_t)t * E + e] = v[et];
-    }
-    if constexpr (HIST)
-      topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w, tile_bits,
-                            tile_sel, tl);
-    else
-      topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w);
-  }
+  if constexpr (HIST)
+    topk_select_write<ET, true>(v, t, T, E, k, topk_idx, topk_w, tile_bits,
+                                tile_sel, tl);
+  else
+    topk_select_write<ET, true>(v, t, T, E, k, topk_idx, topk_w);
   if constexpr (HIST) {
     __syncthreads();
     for (int e = tid; e < E; e += NT)
       tile_base[(size_t)blockIdx.x * E + e] = __popcll(tile_bits[e]);
     const int n = min(64, T - t0) * k;
     for (int q = tid; q < n; q += NT) {
-      const int tl = q / k, j = q - tl * k;
-      const int e = tile_sel[tl * MOE_MAX_TOPK + j];
+      const int tq = q / k, j = q - tq * k;
+      const int e = tile_sel[tq * MOE_MAX_TOPK + j];
       slot_rank[(size_t)t0 * k + q] =
-          __popcll(tile_bits[e] & ((1ull << tl) - 1ull));
+          __popcll(tile_bits[e] & ((1ull << tq) - 1ull));
     }
   }
 }
 
-// ------------------------------------------------------------------ gate, E < 64
-
-// One workgroup = 16 tokens; the 4 waves split the hidden dimension into
-// 32-aligned quarters, read both operands straight from global memory (the
-// gate weight is small and cache-resident) and reduce through LDS in wave
-// order 0,1,2,3.
 template <typename XT, int ET>
 __global__ __launch_bounds__(256) void gate_topk_ksplit_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w,
@@ -1290,9 +1310,11 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     else if (epw == 6) MOE_GATE_PART(6, TTV, 3);                               \
     else MOE_GATE_PART(8, TTV, 2);                                             \
   } while (0)
+      const int xg = (8 % S == 0 && tiles % (8 / S) == 0) ? 8 / S : 0;
 #define MOE_GATE_LDS(EPWV)                                                     \
-  hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, 4>), pgrid, dim3(512), 0, \
-                     s, x, w, T, H, E, KR, part, done)
+  hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, 4>), dim3(tiles * S),     \
+                     dim3(512), 0, s, x, w, T, H, E, KR, tiles, xg, part,     \
+                     done)
       if (lds_gate) {
         if (epw == 1) MOE_GATE_LDS(1);
         else if (epw == 2) MOE_GATE_LDS(2);
@@ -1332,25 +1354,39 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
         return hipGetLastError();
       }
       // reduction: 64-token workgroups (fused histogram) for many tokens,
-      // 16-token workgroups for few
+      // 16-token workgroups for few; all ranges of a token in flight at
+      // once up to S = 4 (2 for the widest expert counts)
       const bool fuse = T >= 1024;
       const dim3 rgrid(fuse ? (T + 63) / 64 : (T + 15) / 16);
-#define MOE_GATE_RED(ETV, WV, PS)                                              \
-  hipLaunchKernelGGL((gate_reduce_topk_kernel<ETV, WV, PS>), rgrid,           \
-                     dim3(64 * WV), 0, s, part, S, EPS, T, E, k, bias, idx,   \
-                     tw, dbg, tb, sr)
-#define MOE_GATE_RED_E(ETV, WV64, PS64)                                        \
+      const int ch = S == 2 ? 2 : S == 3 ? 3 : epw >= 6 ? 2 : 4;
+#define MOE_GATE_RQ(EPWV, WV, CHV)                                             \
+  hipLaunchKernelGGL((gate_reduce_quad_kernel<EPWV, WV, CHV>), rgrid,         \
+                     dim3(64 * WV), 0, s, part, S, T, E, k, bias, idx, tw,    \
+                     dbg, tb, sr)
+#define MOE_GATE_RQ_W(EPWV, CHV)                                               \
   do {                                                                         \
-    if (fuse) MOE_GATE_RED(ETV, WV64, PS64);                                   \
-    else MOE_GATE_RED(ETV, 4, 1);                                              \
+    if (fuse) MOE_GATE_RQ(EPWV, 16, CHV);                                      \
+    else MOE_GATE_RQ(EPWV, 4, CHV);                                            \
   } while (0)
-      if (epw == 1) MOE_GATE_RED_E(4, 16, 1);
-      else if (epw == 2) MOE_GATE_RED_E(8, 16, 1);
-      else if (epw == 4) MOE_GATE_RED_E(16, 8, 2);
-      else if (epw == 6) MOE_GATE_RED_E(24, 8, 2);
-      else MOE_GATE_RED_E(32, 4, 4);
-#undef MOE_GATE_RED_E
-#undef MOE_GATE_RED
+#define MOE_GATE_RQ_E(EPWV)                                                    \
+  do {                                                                         \
+    if (ch == 2) MOE_GATE_RQ_W(EPWV, 2);                                       \
+    else if (ch == 3) MOE_GATE_RQ_W(EPWV, 3);                                  \
+    else MOE_GATE_RQ_W(EPWV, 4);                                               \
+  } while (0)
+      if (epw == 1) MOE_GATE_RQ_E(1);
+      else if (epw == 2) MOE_GATE_RQ_E(2);
+      else if (epw == 4) MOE_GATE_RQ_E(4);
+      else if (epw == 6) {
+        if (ch == 3) MOE_GATE_RQ_W(6, 3);
+        else MOE_GATE_RQ_W(6, 2);
+      } else {
+        if (ch == 3) MOE_GATE_RQ_W(8, 3);
+        else MOE_GATE_RQ_W(8, 2);
+      }
+#undef MOE_GATE_RQ_E
+#undef MOE_GATE_RQ_W
+#undef MOE_GATE_RQ
       *stage = fuse ? kRouteNeedScan : kRouteNeedPlan;
       return hipGetLastError();
     }
