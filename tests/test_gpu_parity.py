@@ -58,6 +58,13 @@ SMALL = {
     "lds_gate_t4096_e64": C["mixtral"].with_shape(T=4096, H=384, E=64, k=4,
                                                   pad=16),
     "gate_t4096_h1032": C["dsv3_decode"].with_shape(T=4096, H=1032, E=256),
+    # the reduction's range chunks (S = 8 in chunks of 4, and of 2 for 24
+    # and 32 expert tiles) and its 16-token workgroups (512 < T < 1024)
+    "reduce_t2048_s8": C["dsv3_prefill"].with_shape(T=2048, H=1024),
+    "reduce_t2048_e384_s8": C["moonep_skew"].with_shape(T=2048, H=1024),
+    "reduce_t1024_e512_s4": C["moonep_skew"].with_shape(T=1024, H=512, E=512,
+                                                        zipf_bias=False),
+    "reduce_t700_e256": C["dsv3_decode"].with_shape(T=700, H=1024),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 
