@@ -23,13 +23,13 @@
 //    lane and block, 8-byte bf16 stores.
 //  * A workgroup computes a 128x256 tile with 8 waves (two per SIMD, 64x64
 //    each; 256-row tiles need more registers than a wave has and spill);
-//    operands are staged through two LDS stages in MFMA fragment order,
-//    loaded through registers (direct global->LDS copies measured slower on
-//    this part).  Global loads are coalesced (8 lanes per 128-byte row
-//    segment) and scattered into fragment order in LDS with an XOR swizzle
-//    that keeps writes and fragment reads free of bank conflicts: with one
-//    row per lane the address unit handled every 16-byte access separately
-//    and was 72% busy.
+//    operands are staged through two LDS stages, loaded through registers
+//    (direct global->LDS copies measured slower on this part).  Global
+//    loads are coalesced (8 lanes per 128-byte row segment; with one row
+//    per lane the address unit handled every 16-byte access separately and
+//    was 72% busy) and stored row by row in LDS with an XOR swizzle of the
+//    16-byte pieces that keeps both those writes and the fragment reads free
+//    of bank conflicts.
 //  * Work order: all column tiles of one row tile are consecutive, so the
 //    row tile's activations stay cached while the expert's weights stream.
 //  * Row tiles come from a tile map built on the device from offsets, so no
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
 // columns 64 wn .. +64, i.e. TMR/32 x 4 MFMA tiles.  Per 128-wide block each
 // wave loads TMR/128 row groups of the activation tile, two of the weight
 // tile (16 rows x 128 bytes each) and its rows' scales into registers two
-// blocks ahead and writes them to LDS one block ahead, in MFMA fragment
-// order so every ds_read_b128 is conflict-free (two LDS stages).  Per
+// blocks ahead and writes them to LDS one block ahead (two LDS stages),
+// swizzled so that every ds_write_b128 and ds_read_b128 is conflict-free.  Per
 // activation fragment, 4 MFMAs are issued back to back into separate result
 // registers and then scaled into the fp32 accumulators, so one wave's
 // scaling runs while the other wave's MFMAs occupy the matrix core.  A tile
@@ -157,19 +157,21 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   }
 
   // Copies are coalesced: a 16-row x 128-byte group is two loads of 8 rows,
-  // 8 lanes per row reading its 128 bytes (piece p = lane & 7).  Each piece
-  // is written to its place in MFMA fragment order: piece p of row r16 is
-  // half p & 1 of the fragment of lane r16 + 16 (p >> 1).  Fragment slots
-  // are XOR-swizzled within their 16-slot bank row so that both these
-  // writes and the fragment reads are free of LDS bank conflicts.
-  auto slot_ofs = [](int h, int m, int c) {          // byte offset in a group
-    return h * 1024 + (16 * m + (c ^ (4 * m) ^ (2 * h))) * 16;
+  // 8 lanes per row reading its 128 bytes (piece p = lane & 7).  In LDS a
+  // group keeps its rows in order, 128 bytes each, with 16-byte piece p of
+  // row r at slot p ^ swz(r); the fragment of lane (g, c) is pieces 2g and
+  // 2g + 1 of row c.  This swizzle keeps both the 16-byte writes (8 lanes
+  // per row) and the fragment reads (16 lanes, 16 rows) free of LDS bank
+  // conflicts on gfx950 (a fragment-order layout measured 2-way conflicts on
+  // its writes, half of the kernel's LDS cycles).
+  auto row_ofs = [](int r, int p) {                  // byte offset in a group
+    return r * 128 + ((p ^ ((r & 7) ^ ((r >> 3) & 1))) * 16);
   };
   const int lp = lane & 7, lr = lane >> 3;
   int wofs[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) wofs[u] = slot_ofs(lp & 1, lp >> 1, 8 * u + lr);
-  const int rofs0 = slot_ofs(0, g4, c16), rofs1 = slot_ofs(1, g4, c16);
+  for (int u = 0; u < 2; ++u) wofs[u] = row_ofs(8 * u + lr, lp);
+  const int rofs0 = row_ofs(c16, 2 * g4), rofs1 = row_ofs(c16, 2 * g4 + 1);
   // this lane's sources (block 0) as 32-bit byte offsets from uniform
   // bases (cap * K and N * K fit in 32 bits); block b adds b * 128
   const unsigned char* wexp = w + (size_t)e * N * K;
