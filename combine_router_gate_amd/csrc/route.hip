@@ -89,6 +89,14 @@ __device__ __forceinline__ f32x4 mfma_step(const Frag<float>& a,
   return c;
 }
 
+// Slot of 16-byte piece p of row r in a row-major LDS tile of 128-byte rows
+// is p ^ gate_lds_swz(r): the coalesced writes (8 lanes per row) and the
+// fragment reads (16 rows, one piece) then touch distinct banks on gfx950,
+// whose ds_*_b128 grouping a plain p ^ (r & 7) leaves 2-way conflicted.
+__device__ __forceinline__ int gate_lds_swz(int r) {
+  return (r & 7) ^ ((r >> 3) & 1);
+}
+
 // ------------------------------------------------------------------ top-k
 
 // Top-k of one token per 16-lane group.  Lane c of the group holds the
@@ -323,6 +331,7 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
   constexpr int KS = 32 * PQ;              // k per super-step
   constexpr int RB = 2 * KS;               // bytes of one x row per step
   constexpr int NP = 4 * PQ;               // 16-byte pieces per row
+  static_assert(NP == 8, "the LDS swizzle assumes 128-byte rows");
   constexpr int XSLOT = 64 * RB;           // bytes of one x slot
   constexpr int LDS_BYTES = (64 * LROW * 4 > 2 * XSLOT) ? 64 * LROW * 4 : 2 * XSLOT;
   __shared__ __align__(16) unsigned char lds[LDS_BYTES];
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 #pragma unroll
       for (int q = 0; q < PQ; ++q) {
         const bool ok = xrow_ok && i * KS + (xp + q) * 8 < H;
-        st16(slot + xr * RB + (((xp + q) ^ (xr & (NP - 1))) * 16),
+        st16(slot + xr * RB + (((xp + q) ^ gate_lds_swz(xr)) * 16),
              ok ? xreg[j][q] : z);
       }
       lds_barrier();
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
           const int r = tt * 16 + c16;
           const int p = g * PQ + q;
           Frag<uint16_t> a;
-          a.v = *reinterpret_cast<const u32x4*>(slot + r * RB + ((p ^ (r & (NP - 1))) * 16));
+          a.v = *reinterpret_cast<const u32x4*>(slot + r * RB + ((p ^ gate_lds_swz(r)) * 16));
 #pragma unroll
           for (int et = 0; et < EPW; ++et) {
             Frag<uint16_t> b;
@@ -475,6 +484,7 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
   constexpr int KS = 32 * PQ;              // k per super-step
   constexpr int RB = 2 * KS;               // bytes of one x row per step
   constexpr int NP = 4 * PQ;               // 16-byte pieces per row
+  static_assert(NP == 8, "the LDS swizzle assumes 128-byte rows");
   constexpr int XSLOT = TTOK * RB;         // bytes of one x slot
   constexpr int XPT = TTOK * NP / 256;     // x pieces per thread per step
   static_assert(XPT >= 1 && TTOK * NP % 256 == 0, "tile too small");
@@ -549,7 +559,7 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
 #pragma unroll
       for (int m = 0; m < XPT; ++m) {
         const bool ok = xrow_ok[m] && k_lo + i * KS + xp[m] * 8 < k_hi;
-        st16(slot + xr[m] * RB + ((xp[m] ^ (xr[m] & (NP - 1))) * 16),
+        st16(slot + xr[m] * RB + ((xp[m] ^ gate_lds_swz(xr[m])) * 16),
              ok ? xreg[jx][m] : z);
       }
       lds_barrier();
@@ -561,7 +571,7 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
           const int r = tt * 16 + c16;
           const int p = g * PQ + q;
           Frag<uint16_t> a;
-          a.v = *reinterpret_cast<const u32x4*>(slot + r * RB + ((p ^ (r & (NP - 1))) * 16));
+          a.v = *reinterpret_cast<const u32x4*>(slot + r * RB + ((p ^ gate_lds_swz(r)) * 16));
 #pragma unroll
           for (int et = 0; et < EPW; ++et) {
             Frag<uint16_t> b;
@@ -597,14 +607,9 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
 // block b+1 is written into the other.  The 2-block loop has no branches
 // and its loads are unconditional (clamped to the range), which keeps the
 // compiler's wait counts exact instead of draining every load each
-// iteration.  Rows are XOR-swizzled in LDS by gate_lds_swz so that both the
-// coalesced 16-byte writes and the fragment reads hit distinct banks.
+// iteration.  Rows are XOR-swizzled in LDS by gate_lds_swz.
 // Requires every range to be whole 128-element pairs of blocks
 // (H % 128 == 0, KR % 128 == 0) and byte offsets below 2^32.
-__device__ __forceinline__ int gate_lds_swz(int r) {
-  return (r & 7) ^ ((r >> 3) & 1);
-}
-
 template <int EPW, int TT>
 __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
