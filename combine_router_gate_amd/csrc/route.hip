@@ -1358,10 +1358,12 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
         *stage = kRouteDone;
         return hipGetLastError();
       }
-      // reduction: 64-token workgroups (fused histogram) for many tokens,
-      // 16-token workgroups for few; all ranges of a token in flight at
-      // once up to S = 4 (2 for the widest expert counts)
-      const bool fuse = T >= 1024;
+      // reduction: 64-token workgroups that also build the tile histogram
+      // once they alone fill every CU (its top-k is VALU-bound, so fewer
+      // workgroups leave CUs idle), otherwise 16-token workgroups and a
+      // separate histogram pass; all ranges of a token in flight at once up
+      // to S = 4 (2 for the widest expert counts)
+      const bool fuse = (T + 63) / 64 >= 256;
       const dim3 rgrid(fuse ? (T + 63) / 64 : (T + 15) / 16);
       const int ch = S == 2 ? 2 : S == 3 ? 3 : epw >= 6 ? 2 : 4;
 #define MOE_GATE_RQ(EPWV, WV, CHV)                                             \
