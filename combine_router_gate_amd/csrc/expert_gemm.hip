@@ -95,10 +95,12 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
 // A workgroup computes a TMR (rows, 128 or 256) x 256 (columns) tile with 8
 // waves (two per SIMD); wave (wm, wn) owns rows TMR/2 wm .. +TMR/2 and
 // columns 64 wn .. +64, i.e. TMR/32 x 4 MFMA tiles.  Per 128-wide block each
-// wave loads TMR/128 row groups of the activation tile, two of the weight
-// tile (16 rows x 128 bytes each) and its rows' scales into registers two
-// blocks ahead and writes them to LDS one block ahead (two LDS stages),
-// swizzled so that every ds_write_b128 and ds_read_b128 is conflict-free.  Per
+// wave loads TMR/128 row groups of the activation tile and two of the
+// weight tile (16 rows x 128 bytes each) into registers two blocks ahead and
+// writes them to LDS one block ahead (two LDS stages), swizzled so that
+// every ds_write_b128 and ds_read_b128 is conflict-free.  The activation
+// scales of the tile's rows, all blocks, are copied to LDS once at the start
+// (one scattered 4-byte load per row and block measured slower).  Per
 // activation fragment, 4 MFMAs are issued back to back into separate result
 // registers and then scaled into the fp32 accumulators, so one wave's
 // scaling runs while the other wave's MFMAs occupy the matrix core.  A tile
@@ -107,8 +109,7 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
 constexpr int kTN = 256;
 template <int TMR> struct GemmTile {
   static constexpr int A = TMR * 128, B = kTN * 128;
-  static constexpr int S = 8 * (TMR / 2) * 4;       // each wave's rows' scales
-  static constexpr int Stage = A + B + S;
+  static constexpr int Stage = A + B;
   static constexpr int MI = TMR / 32;               // row fragments per wave
   static constexpr int AG = TMR / 128;              // row groups copied per wave
 };
@@ -126,6 +127,10 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::Stage];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::Stage];
   __shared__ float sw[2][kGemmMaxK / 128];
+  // the tile's activation scales, all blocks (row stride padded by one float
+  // so the 16 rows of a fragment read distinct banks)
+  constexpr int kRS = kGemmMaxK / 128 + 1;
+  __shared__ float rsc[TMR * kRS];
   const int bid = blockIdx.x;
   const int ng = bid / (mt_ub * gn);
   const int rem = bid - ng * mt_ub * gn;
@@ -149,11 +154,18 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   // this wave's row half holds rows of the segment (uniform per wave)
   const bool half_live = (TMR / 2) * wm < r_end - r0;
 
-  // weight scales of the tile's two 128-column blocks
+  // weight scales of the tile's two 128-column blocks, and the activation
+  // scales of its rows (one coalesced copy of TMR * KB consecutive floats;
+  // rows past the segment repeat its last row and are never stored)
   for (int i = tid; i < 2 * KB; i += 512) {
     const int h = i / KB, b = i - h * KB;
     const int nb = nt * 2 + h < NB ? nt * 2 + h : NB - 1;
     sw[h][b] = wscale[((size_t)e * NB + nb) * KB + b];
+  }
+  for (int i = tid; i < TMR * KB; i += 512) {
+    const int rr = i / KB, b = i - rr * KB;
+    const int r = r0 + rr < r_end ? r0 + rr : r_end - 1;
+    rsc[rr * kRS + b] = rscale[(size_t)r * KB + b];
   }
 
   // Copies are coalesced: a 16-row x 128-byte group is two loads of 8 rows,
@@ -197,15 +209,6 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
       n = n < N ? n : N - 1;
       boff[q][u] = (uint32_t)n * (uint32_t)K + 16 * lp;
     }
-  // row scales: every wave copies the rows it multiplies into its own slot
-  const float* ssrc[G::AG];
-#pragma unroll
-  for (int q = 0; q < G::AG; ++q) {
-    int srow = r0 + (TMR / 2) * wm + 64 * q + lane;
-    srow = srow < r_end ? srow : r_end - 1;
-    ssrc[q] = rscale + (size_t)srow * KB;
-  }
-  const int scopy = wv * (TMR / 2);
 
   f32x4 acc[G::MI][4];
 #pragma unroll
@@ -216,7 +219,6 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   // staging through registers: block b + 1 is loaded during block b - 1 and
   // written to LDS at the start of block b
   u32x4 ra_[G::AG][2], rb_[2][2];
-  float rs_[G::AG];
   auto load_regs = [&](int b) {
     const size_t o = (size_t)b * 128;
 #pragma unroll
@@ -229,8 +231,6 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int u = 0; u < 2; ++u) rb_[q][u] = ld16(wexp + boff[q][u] + o);
-#pragma unroll
-    for (int q = 0; q < G::AG; ++q) rs_[q] = ssrc[q][b];
   };
   auto store_regs = [&](unsigned char* base) {
 #pragma unroll
@@ -247,9 +247,6 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
       for (int u = 0; u < 2; ++u)
         *reinterpret_cast<u32x4*>(base + G::A + (2 * wv + q) * 2048 +
                                   wofs[u]) = rb_[q][u];
-#pragma unroll
-    for (int q = 0; q < G::AG; ++q)
-      ((float*)(base + G::A + G::B))[scopy + 64 * q + lane] = rs_[q];
   };
 
   auto block = [&](int b, const unsigned char* base, unsigned char* next1) {
@@ -260,7 +257,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     store_regs(next1);
     load_regs(b + 2 < KB ? b + 2 : KB - 1);
     if (!half_live) return;
-    const float* sa = (const float*)(base + G::A + G::B) + scopy;
+    const float* sa = rsc + ((TMR / 2) * wm) * kRS + b;
     const float swb = sw[wn >> 1][b];
     i32x8 fb[4];
 #pragma unroll
@@ -278,7 +275,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
       const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + rofs1);
       const i32x8 fa = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const float si = sa[16 * i + c16] * swb;
+      const float si = sa[(16 * i + c16) * kRS] * swb;
       f32x4 p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
