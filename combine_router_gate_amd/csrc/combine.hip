@@ -306,23 +306,28 @@ __global__ __launch_bounds__(1024) void combine_backward_kernel(
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) dot[j] = 0.0f;
   for (int c = p * 64 + lane; c < nc8; c += hs * 64) {
+    // the gradient chunk and all k row chunks are loaded before any of them
+    // is used, so they are in flight together
+    const u32x4 gv = ld16_stream(g + trow + (size_t)c * 16);
+    Chunk8<YT> yv[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (rj[j] >= 0) {
+        const unsigned char* yr = y + (size_t)rj[j] * yrowb;
+        if constexpr (YT == 1) {
+          yv[j].a = ld16(yr + (size_t)c * 16);
+        } else {
+          yv[j].a = ld16(yr + (size_t)c * 32);
+          yv[j].b = ld16(yr + (size_t)c * 32 + 16);
+        }
+      }
     float gf[8];
-    unpack8_bf16(ld16_stream(g + trow + (size_t)c * 16), gf);
+    unpack8_bf16(gv, gf);
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (rj[j] < 0) continue;
       float yf[8], d[8];
-      if constexpr (YT == 1) {
-        unpack8_bf16(ld16(y + (size_t)rj[j] * yrowb + (size_t)c * 16), yf);
-      } else {
-        const u32x4 a = ld16(y + (size_t)rj[j] * yrowb + (size_t)c * 32);
-        const u32x4 b = ld16(y + (size_t)rj[j] * yrowb + (size_t)c * 32 + 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          yf[i] = __uint_as_float(a[i]);
-          yf[4 + i] = __uint_as_float(b[i]);
-        }
-      }
+      unpack8<YT>(yv[j], yf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         dot[j] = fmaf(gf[i], yf[i], dot[j]);

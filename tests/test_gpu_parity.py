@@ -58,6 +58,9 @@ SMALL = {
     "lds_gate_t4096_e64": C["mixtral"].with_shape(T=4096, H=384, E=64, k=4,
                                                   pad=16),
     "gate_t4096_h1032": C["dsv3_decode"].with_shape(T=4096, H=1032, E=256),
+    # 34 tiles of 128 tokens (the last ragged), S = 4: workgroups mapped so
+    # each XCD serves one hidden range
+    "lds_gate_t4300_xcd": C["dsv3_prefill"].with_shape(T=4300, H=1024),
     # the reduction's range chunks (S = 8 in chunks of 4, and of 2 for 24
     # and 32 expert tiles) and its 16-token workgroups (512 < T < 1024)
     "reduce_t2048_s8": C["dsv3_prefill"].with_shape(T=2048, H=1024),
