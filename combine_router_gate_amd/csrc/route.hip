@@ -17,7 +17,8 @@
 //    softmax and top-k run on-chip and the logits never touch HBM.
 //  * E >= 64: a workgroup of 4 waves covers 64 tokens and stages the gate
 //    weight through LDS in 128-byte k-chunks shared by the 4 waves; x is
-//    streamed once with non-temporal loads.
+//    read once with ordinary (allocating) loads, so the dispatch that reads
+//    it next finds much of it still in the memory-attached cache.
 //  * E < 64 (memory-bound gate): the 4 waves split the hidden dimension of a
 //    16-token tile and reduce their partial logits through LDS in a fixed
 //    order, so four times as many workgroups stream x.
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256) void gate_topk_wide_kernel(
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int kk = kc + s * 32 + g * 8;
-      frag_load<XT>(anext[s], xrow + kk, arow_ok && kk < H, true);
+      frag_load<XT>(anext[s], xrow + kk, arow_ok && kk < H, false);
     }
   };
 
@@ -302,10 +303,10 @@ __global__ __launch_bounds__(256) void gate_topk_wide_kernel(
 // per 16x16x32 MFMA; x and W use the same (g, piece) -> k map, so each lane
 // reads 64 contiguous bytes of every row it touches.
 //  * x: the workgroup loads the [64 tokens x 128 k] tile (16 KB, 64 B per
-//    thread, non-temporal) D super-steps ahead into a register ring and
-//    stores it into one of two LDS slots right before use.  Within a slot,
-//    16-byte piece p of row r sits at position p ^ (r & 15), so the 16 rows
-//    read by an MFMA operand fall into distinct banks.
+//    thread) D super-steps ahead into a register ring and stores it into one
+//    of two LDS slots right before use.  Within a slot, 16-byte piece p of
+//    row r sits at position p ^ gate_lds_swz(r), so the 16 rows read by an
+//    MFMA operand fall into distinct banks.
 //  * W: each wave loads its own B fragments from global memory (the gate
 //    weight stays L2-resident while x streams past it) into a D-deep
 //    register ring.
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 #pragma unroll
     for (int q = 0; q < PQ; ++q) {
       const int kk = i * KS + (xp + q) * 8;
-      dst[q] = ld16_stream(xrow + (kk < H ? kk : H - 8));
+      dst[q] = ld16(xrow + (kk < H ? kk : H - 8));
     }
   };
   auto load_w = [&](int i, u32x4 (&dst)[EPW][PQ]) {
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
 #pragma unroll
     for (int m = 0; m < XPT; ++m) {
       const int kk = k_lo + i * KS + xp[m] * 8;
-      dst[m] = ld16_stream(xsrc[m] + (kk < H ? kk : H - 8));
+      dst[m] = ld16(xsrc[m] + (kk < H ? kk : H - 8));
     }
   };
   auto load_w = [&](int i, u32x4 (&dst)[EPW][PQ]) {
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
   auto load_x = [&](int b, u32x4 (&dst)[XPT]) {
     const uint32_t kb = (uint32_t)min(b, nb - 1) * 128u;
 #pragma unroll
-    for (int m = 0; m < XPT; ++m) dst[m] = ld16_stream(xb + xo[m] + kb);
+    for (int m = 0; m < XPT; ++m) dst[m] = ld16(xb + xo[m] + kb);
   };
   auto load_w = [&](int b) {
     const uint32_t kb = (uint32_t)min(b, nb - 1) * 128u;
@@ -879,7 +880,7 @@ __global__ __launch_bounds__(256) void gate_topk_ksplit_kernel(
     for (int u = 0; u < U; ++u) {
       const int kk = k0 + u * 32 + g * 8;
       const bool kok = kk < k_hi;
-      frag_load<XT>(a[u], xrow + kk, arow_ok && kok, true);
+      frag_load<XT>(a[u], xrow + kk, arow_ok && kok, false);
 #pragma unroll
       for (int et = 0; et < ET; ++et)
         frag_load<XT>(b[u][et], wrow[et] + kk, wrow_ok[et] && kok, false);
