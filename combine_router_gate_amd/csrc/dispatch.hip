@@ -55,7 +55,7 @@ __device__ __forceinline__ int token_row(
 
 // MODE 0: exact copy (x and payload of the same 2- or 4-byte type)
 // MODE 1: bf16 x -> fp8;  MODE 2: fp32 x -> fp8
-template <int KMAX, int MODE, bool CACHED>
+template <int KMAX, int MODE>
 __global__ __launch_bounds__(256) void dispatch_kernel(
     const unsigned char* __restrict__ x, int esize, int T, int H,
     const int32_t* __restrict__ topk_idx, int k, int E,
@@ -108,9 +108,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * 64 + lane;
-        if (c < nc)
-          v[u] = CACHED ? ld16(src + (size_t)c * 16)
-                        : ld16_stream(src + (size_t)c * 16);
+        if (c < nc) v[u] = ld16_stream(src + (size_t)c * 16);
       }
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
@@ -140,8 +138,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
         const int c = c0 + u * 64 + lane;
         const unsigned char* p = src + (size_t)(c < nc16 ? c : nc16 - 1) * EB;
 #pragma unroll
-        for (int q = 0; q < EB / 16; ++q)
-          v[u][q] = CACHED ? ld16(p + 16 * q) : ld16_stream(p + 16 * q);
+        for (int q = 0; q < EB / 16; ++q) v[u][q] = ld16_stream(p + 16 * q);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -259,7 +256,7 @@ __global__ __launch_bounds__(256) void fixture_kernel(
 
 // ------------------------------------------------------------------ launchers
 
-template <int KMAX, bool CACHED>
+template <int KMAX>
 static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
                               const unsigned char* x, int esize, int T, int H,
                               const int32_t* idx, int k, int E,
@@ -269,17 +266,17 @@ static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
                               int32_t* row_src, int32_t* tok_row, int tblocks,
                               int hs) {
   if (mode == 0)
-    hipLaunchKernelGGL((dispatch_kernel<KMAX, 0, CACHED>), grid, dim3(256),
-                       0, s, x, esize, T, H, idx, k, E, counts, offsets, tb,
-                       sr, rows, cap, sc, row_src, tok_row, tblocks, hs);
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 0>), grid, dim3(256), 0, s, x,
+                       esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
+                       cap, sc, row_src, tok_row, tblocks, hs);
   else if (mode == 1)
-    hipLaunchKernelGGL((dispatch_kernel<KMAX, 1, CACHED>), grid, dim3(256),
-                       0, s, x, esize, T, H, idx, k, E, counts, offsets, tb,
-                       sr, rows, cap, sc, row_src, tok_row, tblocks, hs);
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 1>), grid, dim3(256), 0, s, x,
+                       esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
+                       cap, sc, row_src, tok_row, tblocks, hs);
   else
-    hipLaunchKernelGGL((dispatch_kernel<KMAX, 2, CACHED>), grid, dim3(256),
-                       0, s, x, esize, T, H, idx, k, E, counts, offsets, tb,
-                       sr, rows, cap, sc, row_src, tok_row, tblocks, hs);
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 2>), grid, dim3(256), 0, s, x,
+                       esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
+                       cap, sc, row_src, tok_row, tblocks, hs);
 }
 
 hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
@@ -304,22 +301,10 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
   const unsigned char* xb = (const unsigned char*)x;
   unsigned char* rb = (unsigned char*)rows;
   const long long cap = (long long)capacity;
-  // x is read with ordinary loads when it fits in half of the 256 MB
-  // memory-attached cache (where the layer that produced it leaves it),
-  // streamed otherwise
-  const bool cached = (size_t)T * H * esize <= kCachedGatherBytes;
 #define MOE_DISPATCH_K(KV)                                                   \
-  do {                                                                       \
-    if (cached)                                                              \
-      launch_dispatch_k<KV, true>(mode, grid, s, xb, esize, T, H, topk_idx,  \
-                                  k, E, counts, offsets, tb, sr, rb, cap,    \
-                                  row_scales, row_src, tok_row, tblocks, hs);\
-    else                                                                     \
-      launch_dispatch_k<KV, false>(mode, grid, s, xb, esize, T, H, topk_idx, \
-                                   k, E, counts, offsets, tb, sr, rb, cap,   \
-                                   row_scales, row_src, tok_row, tblocks,    \
-                                   hs);                                      \
-  } while (0)
+  launch_dispatch_k<KV>(mode, grid, s, xb, esize, T, H, topk_idx, k, E,      \
+                        counts, offsets, tb, sr, rb, cap, row_scales,        \
+                        row_src, tok_row, tblocks, hs)
   if (k <= 1) MOE_DISPATCH_K(1);
   else if (k <= 2) MOE_DISPATCH_K(2);
   else if (k <= 4) MOE_DISPATCH_K(4);
