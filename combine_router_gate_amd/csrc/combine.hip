@@ -32,18 +32,15 @@ template <int YT> struct Chunk8;
 template <> struct Chunk8<1> { u32x4 a; };
 template <> struct Chunk8<0> { u32x4 a, b; };
 
-// CACHED: ordinary loads (the rows may stay in L2 / MALL); otherwise
-// streaming loads that do not displace other data.
-template <int YT, bool CACHED>
+template <int YT>
 __device__ __forceinline__ Chunk8<YT> load8(const unsigned char* __restrict__ row,
                                             int c) {
   Chunk8<YT> v;
   if constexpr (YT == 1) {
-    v.a = CACHED ? ld16(row + (size_t)c * 16) : ld16_stream(row + (size_t)c * 16);
+    v.a = ld16_stream(row + (size_t)c * 16);
   } else {
-    const unsigned char* p = row + (size_t)c * 32;
-    v.a = CACHED ? ld16(p) : ld16_stream(p);
-    v.b = CACHED ? ld16(p + 16) : ld16_stream(p + 16);
+    v.a = ld16_stream(row + (size_t)c * 32);
+    v.b = ld16_stream(row + (size_t)c * 32 + 16);
   }
   return v;
 }
@@ -65,8 +62,7 @@ __device__ __forceinline__ void unpack8(const Chunk8<YT>& v, float f[8]) {
 // farskip_aux_kernel).
 // Each lane keeps U = 2 groups of 8 elements in flight: for k = 8 that is
 // 2 * (8 gathers + shared + residual) 16-byte loads issued before any math.
-// CACHED selects ordinary loads for the gathered rows (see launch_combine).
-template <int KMAX, int YT, int OUT, bool CACHED>
+template <int KMAX, int YT, int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const unsigned char* __restrict__ y, long long y_rows, int H,
     const int32_t* __restrict__ tok_row, const float* __restrict__ topk_w,
@@ -112,8 +108,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
       if (c < nc8) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
-          if (rj[j] >= 0)
-            g[u][j] = load8<YT, CACHED>(y + (size_t)rj[j] * yrowb, c);
+          if (rj[j] >= 0) g[u][j] = load8<YT>(y + (size_t)rj[j] * yrowb, c);
         shv[u] = shared != nullptr ? ld16_stream(shared + trow + (size_t)c * 16) : z;
         if constexpr (OUT == 0 || OUT == 3)
           rsv[u] = ld16(res_in + trow + (size_t)c * 16);
@@ -169,7 +164,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
-template <int KMAX, int YT, bool CACHED>
+template <int KMAX, int YT>
 static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                              const unsigned char* y, long long y_rows, int H,
                              const int32_t* tok_row, const float* w, int T,
@@ -177,21 +172,17 @@ static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                              const unsigned char* ri, unsigned char* ro,
                              unsigned char* rn, unsigned char* out, int hs) {
   if (om == 0)
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 0, CACHED>), grid, dim3(256),
-                       0, s, y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn,
-                       out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 0>), grid, dim3(256), 0, s, y,
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else if (om == 3)
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 3, CACHED>), grid, dim3(256),
-                       0, s, y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn,
-                       out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 3>), grid, dim3(256), 0, s, y,
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else if (om == 1)
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 1, CACHED>), grid, dim3(256),
-                       0, s, y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn,
-                       out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 1>), grid, dim3(256), 0, s, y,
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 2, CACHED>), grid, dim3(256),
-                       0, s, y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn,
-                       out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 2>), grid, dim3(256), 0, s, y,
+                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
 }
 
 // Waves per token: enough waves in flight for few tokens (about 2048),
@@ -218,25 +209,14 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
   unsigned char* rn = (unsigned char*)rnr;
   unsigned char* ob = (unsigned char*)out;
   const long long yr = (long long)y_rows;
-  // Rows read with ordinary loads when they fit in half of the 256 MB
-  // memory-attached last-level cache (an expert GEMM that has just written
-  // them leaves them there); a larger set is streamed so that it does not
-  // displace everything else on its way through.
-  const bool cached = (size_t)T * k * H * (ydt == DT_BF16 ? 2 : 4) <=
-                      kCachedGatherBytes;
-#define MOE_COMB_C(KV, YV)                                                    \
-  do {                                                                        \
-    if (cached)                                                               \
-      launch_combine_k<KV, YV, true>(om, grid, s, yb, yr, H, tok_row, topk_w, \
-                                     T, k, sh, ri, ro, rn, ob, hs);           \
-    else                                                                      \
-      launch_combine_k<KV, YV, false>(om, grid, s, yb, yr, H, tok_row,        \
-                                      topk_w, T, k, sh, ri, ro, rn, ob, hs);  \
-  } while (0)
 #define MOE_COMB(KV)                                                          \
   do {                                                                        \
-    if (ydt == DT_BF16) MOE_COMB_C(KV, 1);                                    \
-    else MOE_COMB_C(KV, 0);                                                   \
+    if (ydt == DT_BF16)                                                       \
+      launch_combine_k<KV, 1>(om, grid, s, yb, yr, H, tok_row, topk_w, T, k,  \
+                              sh, ri, ro, rn, ob, hs);                        \
+    else                                                                      \
+      launch_combine_k<KV, 0>(om, grid, s, yb, yr, H, tok_row, topk_w, T, k,  \
+                              sh, ri, ro, rn, ob, hs);                        \
   } while (0)
   if (k <= 1) MOE_COMB(1);
   else if (k <= 2) MOE_COMB(2);
@@ -244,7 +224,6 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
   else if (k <= 8) MOE_COMB(8);
   else MOE_COMB(16);
 #undef MOE_COMB
-#undef MOE_COMB_C
   return hipGetLastError();
 }
 

@@ -47,9 +47,6 @@ inline size_t ws_partial_bytes(int T, int E) {
 }
 // Up to this many tokens, histogram, scan and ranks run in one workgroup.
 constexpr int kSmallPlanT = 512;
-// Row sets up to this size are read with ordinary (cached) loads, larger
-// ones with streaming loads: half of the 256 MB memory-attached cache.
-constexpr size_t kCachedGatherBytes = size_t(128) << 20;
 inline size_t workspace_bytes(int T, int E, int k) {
   return T == 0 ? 0
                 : ws_tile_bytes(T, E) + ws_rank_bytes(T, k) +
