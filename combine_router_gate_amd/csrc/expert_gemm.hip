@@ -29,7 +29,8 @@
 //    per lane the address unit handled every 16-byte access separately and
 //    was 72% busy) and stored row by row in LDS with an XOR swizzle of the
 //    16-byte pieces that keeps both those writes and the fragment reads free
-//    of bank conflicts.
+//    of bank conflicts.  The activation scales of the tile's rows, for all
+//    K blocks, are copied to LDS once at its start with coalesced loads.
 //  * Work order: all column tiles of one row tile are consecutive, so the
 //    row tile's activations stay cached while the expert's weights stream.
 //  * Row tiles come from a tile map built on the device from offsets, so no

@@ -13,12 +13,17 @@
 // Design for CDNA4:
 //  * Gate GEMM l = x W^T on the matrix cores: v_mfma_f32_16x16x32_bf16 for
 //    bf16 inputs, v_mfma_f32_16x16x4_f32 for fp32 inputs, fp32 accumulation.
-//    A wave owns a 16-token x (16*ET)-expert block of logits in registers, so
-//    softmax and top-k run on-chip and the logits never touch HBM.
-//  * E >= 64: a workgroup of 4 waves covers 64 tokens and stages the gate
-//    weight through LDS in 128-byte k-chunks shared by the 4 waves; x is
-//    read once with ordinary (allocating) loads, so the dispatch that reads
-//    it next finds much of it still in the memory-attached cache.
+//    Softmax and top-k run on-chip, so the logits never touch HBM (only fp32
+//    partial sums of a split hidden dimension do).
+//  * E >= 64, bf16: the hidden dimension is split into S ranges so that
+//    about 256 workgroups run; gate_partial_lds_kernel (4096 tokens and
+//    more: 128 tokens x all experts per workgroup, both operands staged
+//    through LDS) or gate_partial_kernel writes the partial logits, and
+//    gate_reduce_quad_kernel (gate_reduce_plan_small_kernel up to 512
+//    tokens) sums them in range order and selects the top-k.  Where a split
+//    would not pay, gate_topk_v2_kernel does all of it in one pass.  x is
+//    read with ordinary (allocating) loads, so the dispatch that reads it
+//    next finds much of it still in the memory-attached cache.
 //  * E < 64 (memory-bound gate): the 4 waves split the hidden dimension of a
 //    16-token tile and reduce their partial logits through LDS in a fixed
 //    order, so four times as many workgroups stream x.
