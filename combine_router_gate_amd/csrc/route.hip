@@ -853,7 +853,10 @@ __global__ __launch_bounds__(256) void gate_topk_ksplit_kernel(
     const float* __restrict__ bias, int T, int H, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits_dbg) {
-  constexpr int U = 4;  // k steps in flight per wave
+  // k steps in flight per wave: a workgroup per 16 tokens leaves one per
+  // CU, so each must keep enough of its x stream in flight on its own
+  // (4 steps, 16 KB per CU, held the stream to ~2 TB/s)
+  constexpr int U = sizeof(XT) == 2 ? 16 : 8;
   __shared__ f32x4 red[3][ET][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
