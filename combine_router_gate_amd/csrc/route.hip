@@ -1268,7 +1268,10 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
                                     hipStream_t s) {
   *stage = kRouteNeedPlan;
   const int et = (E + 15) / 16;
-  if (et <= 2) {
+  // few experts: the k-split single pass, except for many bf16 tokens,
+  // where the LDS-staged split gate streams x faster
+  const bool few_lds = sizeof(XT) == 2 && T >= 4096 && H % 128 == 0;
+  if (et <= 2 && !few_lds) {
     const dim3 grid((T + 15) / 16);
     if (et == 1)
       hipLaunchKernelGGL((gate_topk_ksplit_kernel<XT, 1>), grid, dim3(256), 0,

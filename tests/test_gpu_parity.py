@@ -61,6 +61,9 @@ SMALL = {
     # 34 tiles of 128 tokens (the last ragged), S = 4: workgroups mapped so
     # each XCD serves one hidden range
     "lds_gate_t4300_xcd": C["dsv3_prefill"].with_shape(T=4300, H=1024),
+    # few experts (E <= 32) and many bf16 tokens take the LDS-staged gate too
+    "lds_gate_t4200_e24": C["mixtral"].with_shape(T=4200, H=512, E=24, k=3,
+                                                  pad=16),
     # the reduction's range chunks (S = 8 in chunks of 4, and of 2 for 24
     # and 32 expert tiles) and its 16-token workgroups (512 < T < 1024)
     "reduce_t2048_s8": C["dsv3_prefill"].with_shape(T=2048, H=1024),
