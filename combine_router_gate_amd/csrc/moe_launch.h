@@ -18,9 +18,9 @@ inline int num_tiles(int T) { return (T + 63) / 64; }
 //   slot_rank [T, k] int32       rank of slot (t, j) among its tile's tokens
 //                                that chose the same expert
 //   partial   [S, T, EP] fp32    partial gate logits when the hidden
-//                                dimension is split S ways (few tokens);
-//                                S * T <= kSplitRows, EP = experts padded to
-//                                the gate kernel's 64 * EPW
+//                                dimension is split S ways (up to kSplitRows
+//                                tokens); S * T <= 2 * kSplitRows, EP =
+//                                experts padded to the gate's 64 * EPW
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 constexpr int kSplitRows = 16384;
 constexpr int kSplitMax = 64;
