@@ -393,8 +393,8 @@ def main():
                     "MiB before timing (reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures the single-GPU transform only: this build "
-              "has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures the single-GPU transform only; there is "
+              "no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

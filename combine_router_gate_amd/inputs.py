@@ -10,9 +10,8 @@ Every tensor is drawn from ``numpy.random.default_rng([seed, tensor_id])``
 bf16 (ties to even).  Tensor ids: x=1, gate weight=2, expert permutation=3,
 expert scales=4, shared-expert output=5, residual=6.
 
-Workload shapes follow the five synthetic configurations of the build
-(Tiny, Mixtral-8x7B-shaped, DeepSeek-V3 decode- and prefill-shaped, and a
-MoonEP-shaped skewed load).  The shapes come from the models the pages name:
+There are five synthetic workloads (Tiny, Mixtral-8x7B-shaped, DeepSeek-V3
+decode- and prefill-shaped, and a MoonEP-shaped skewed load).  The shapes come from the models the pages name:
 Mixtral 8x7B and DeepSeek R1/V3 ("Efficient and Portable Mixture-of-Experts
 Communication", Introduction) and MoonEP's ``Buffer(S, H, K, E, ...)``
 example with H=768, K=8, E=384 and ``token_padding`` 128 ("MoonEP developer
