@@ -1296,7 +1296,9 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
                           (epw <= 4 || epw == 6) &&
                           (size_t)T * H * 2 <= 0xffffffffu &&
                           (size_t)E * H * 2 <= 0xffffffffu;
-    const int TT = lds_gate ? 8
+    // LDS-staged gate: 128-token tiles from 16384 tokens, 64-token tiles
+    // below (more workgroups for a smaller hidden split, so fewer partials)
+    const int TT = lds_gate ? (T >= 16384 ? 8 : 4)
                    : (epw <= 4 && T >= 8192) ? 8 : T >= 2048 ? 4 : 2;
     const int tiles = (T + 16 * TT - 1) / (16 * TT);
     const int target = T >= 2048 ? 256 : 128;
@@ -1328,10 +1330,15 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     else MOE_GATE_PART(8, TTV, 2);                                             \
   } while (0)
       const int xg = (8 % S == 0 && tiles % (8 / S) == 0) ? 8 / S : 0;
-#define MOE_GATE_LDS(EPWV)                                                     \
-  hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, 4>), dim3(tiles * S),     \
+#define MOE_GATE_LDS_T(EPWV, TTV)                                              \
+  hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, TTV>), dim3(tiles * S),   \
                      dim3(512), 0, s, x, w, T, H, E, KR, tiles, xg, part,     \
                      done)
+#define MOE_GATE_LDS(EPWV)                                                     \
+  do {                                                                         \
+    if (TT == 8) MOE_GATE_LDS_T(EPWV, 4);                                      \
+    else MOE_GATE_LDS_T(EPWV, 2);                                              \
+  } while (0)
       if (lds_gate) {
         if (epw == 1) MOE_GATE_LDS(1);
         else if (epw == 2) MOE_GATE_LDS(2);
@@ -1347,6 +1354,7 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
         MOE_GATE_PART_E(2);
       }
 #undef MOE_GATE_LDS
+#undef MOE_GATE_LDS_T
 #undef MOE_GATE_PART_E
 #undef MOE_GATE_PART_X
 #undef MOE_GATE_PART
