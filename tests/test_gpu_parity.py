@@ -71,6 +71,10 @@ SMALL = {
     "reduce_t1024_e512_s4": C["moonep_skew"].with_shape(T=1024, H=512, E=512,
                                                         zipf_bias=False),
     "reduce_t700_e256": C["dsv3_decode"].with_shape(T=700, H=1024),
+    # the most experts (512) with many tokens: split gate with 64-token
+    # tiles, reduction in chunks of two ranges
+    "e512_t4096": C["moonep_skew"].with_shape(T=4096, H=256, E=512, k=8,
+                                              zipf_bias=False),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 
