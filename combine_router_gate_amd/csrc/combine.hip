@@ -14,9 +14,10 @@
 // Design for CDNA4: one wavefront per token (several per token when there
 // are too few tokens to fill the chip).  Lanes 0..k-1 fetch the k
 // (row, weight) pairs, broadcast to scalar registers; each lane then owns
-// two groups of 8 consecutive hidden elements per step and issues all their
-// 16-byte row gathers plus the residual and shared loads before any
-// arithmetic (20 independent loads in flight per lane at k = 8),
+// two groups of 8 consecutive hidden elements per step (one when there are
+// few tokens, to spread a row over more waves) and issues all their 16-byte
+// row gathers plus the residual and shared loads before any arithmetic (20
+// independent loads in flight per lane at k = 8),
 // accumulates in fp32 with j ascending (fmaf), adds shared then residual,
 // rounds once to bf16 with the hardware converter and writes with streaming
 // stores.  No floating-point atomics: every output element is produced by
@@ -60,9 +61,11 @@ __device__ __forceinline__ void unpack8(const Chunk8<YT>& v, float f[8]) {
 // OUT: 0 = dual residual (bf16), 1 = routed-only bf16, 2 = routed-only fp32,
 // 3 = main residual stream only (bf16; the auxiliary stream comes from
 // farskip_aux_kernel).
-// Each lane keeps U = 2 groups of 8 elements in flight: for k = 8 that is
-// 2 * (8 gathers + shared + residual) 16-byte loads issued before any math.
-template <int KMAX, int YT, int OUT>
+// Each lane keeps U groups of 8 elements in flight: for k = 8 and U = 2 that
+// is 2 * (8 gathers + shared + residual) 16-byte loads issued before any
+// math.  U = 1 halves a wave's share of the row, so that few tokens can be
+// spread over twice as many waves.
+template <int KMAX, int YT, int OUT, int U>
 __global__ __launch_bounds__(256) void combine_kernel(
     const unsigned char* __restrict__ y, long long y_rows, int H,
     const int32_t* __restrict__ tok_row, const float* __restrict__ topk_w,
@@ -70,7 +73,6 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const unsigned char* res_in, unsigned char* res_out,
     unsigned char* __restrict__ rnr, unsigned char* __restrict__ out,
     int hsplit) {
-  constexpr int U = 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   // wave -> (token, part): with few tokens, hsplit waves share one token's
   // hidden dimension (interleaved groups of 64*U chunks)
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
-template <int KMAX, int YT>
+template <int KMAX, int YT, int U>
 static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                              const unsigned char* y, long long y_rows, int H,
                              const int32_t* tok_row, const float* w, int T,
@@ -172,17 +174,17 @@ static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                              const unsigned char* ri, unsigned char* ro,
                              unsigned char* rn, unsigned char* out, int hs) {
   if (om == 0)
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 0>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 0, U>), grid, dim3(256), 0, s,
+                       y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else if (om == 3)
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 3>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 3, U>), grid, dim3(256), 0, s,
+                       y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else if (om == 1)
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 1>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 1, U>), grid, dim3(256), 0, s,
+                       y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
   else
-    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 2>), grid, dim3(256), 0, s, y,
-                       y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
+    hipLaunchKernelGGL((combine_kernel<KMAX, YT, 2, U>), grid, dim3(256), 0, s,
+                       y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
 }
 
 // Waves per token: enough waves in flight for few tokens (about 2048),
@@ -198,7 +200,11 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
                           int k, const void* shared, const void* res_in,
                           void* res_out, void* rnr, void* out, int odt,
                           hipStream_t s) {
-  const int hs = waves_per_token(T, (H / 8 + 127) / 128);
+  // two groups of 64 chunks per lane step, or one when that leaves too few
+  // waves for the chip (few tokens)
+  const int groups2 = (H / 8 + 127) / 128;
+  const int u = (long long)T * groups2 >= 2048 ? 2 : 1;
+  const int hs = waves_per_token(T, u == 2 ? groups2 : (H / 8 + 63) / 64);
   const dim3 grid((unsigned)(((long long)T * hs + 3) / 4));
   const int om = res_in != nullptr ? (rnr != nullptr ? 0 : 3)
                                    : (odt == DT_BF16 ? 1 : 2);
@@ -209,14 +215,19 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
   unsigned char* rn = (unsigned char*)rnr;
   unsigned char* ob = (unsigned char*)out;
   const long long yr = (long long)y_rows;
+#define MOE_COMB_U(KV, YV)                                                    \
+  do {                                                                        \
+    if (u == 2)                                                               \
+      launch_combine_k<KV, YV, 2>(om, grid, s, yb, yr, H, tok_row, topk_w, T, \
+                                  k, sh, ri, ro, rn, ob, hs);                 \
+    else                                                                      \
+      launch_combine_k<KV, YV, 1>(om, grid, s, yb, yr, H, tok_row, topk_w, T, \
+                                  k, sh, ri, ro, rn, ob, hs);                 \
+  } while (0)
 #define MOE_COMB(KV)                                                          \
   do {                                                                        \
-    if (ydt == DT_BF16)                                                       \
-      launch_combine_k<KV, 1>(om, grid, s, yb, yr, H, tok_row, topk_w, T, k,  \
-                              sh, ri, ro, rn, ob, hs);                        \
-    else                                                                      \
-      launch_combine_k<KV, 0>(om, grid, s, yb, yr, H, tok_row, topk_w, T, k,  \
-                              sh, ri, ro, rn, ob, hs);                        \
+    if (ydt == DT_BF16) MOE_COMB_U(KV, 1);                                    \
+    else MOE_COMB_U(KV, 0);                                                   \
   } while (0)
   if (k <= 1) MOE_COMB(1);
   else if (k <= 2) MOE_COMB(2);
@@ -224,6 +235,7 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
   else if (k <= 8) MOE_COMB(8);
   else MOE_COMB(16);
 #undef MOE_COMB
+#undef MOE_COMB_U
   return hipGetLastError();
 }
 

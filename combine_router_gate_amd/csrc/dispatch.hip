@@ -55,7 +55,9 @@ __device__ __forceinline__ int token_row(
 
 // MODE 0: exact copy (x and payload of the same 2- or 4-byte type)
 // MODE 1: bf16 x -> fp8;  MODE 2: fp32 x -> fp8
-template <int KMAX, int MODE>
+// U: 64-lane chunks per lane step (2 keeps two loads in flight per lane; 1
+// lets few tokens spread over twice as many waves)
+template <int KMAX, int MODE, int U>
 __global__ __launch_bounds__(256) void dispatch_kernel(
     const unsigned char* __restrict__ x, int esize, int T, int H,
     const int32_t* __restrict__ topk_idx, int k, int E,
@@ -102,7 +104,6 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
     const size_t rowb = (size_t)H * esize;
     const int nc = (int)(rowb / 16);
     const unsigned char* src = x + (size_t)t * rowb;
-    constexpr int U = 2;
     for (int c0 = part * 64 * U; c0 < nc; c0 += hsplit * 64 * U) {
       u32x4 v[U];
 #pragma unroll
@@ -122,12 +123,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
       }
     }
   } else {
-    // 16 consecutive elements per lane; 8 lanes per 128-element block; two
-    // 64-lane chunks per iteration, both loaded before either is used, with
+    // 16 consecutive elements per lane; 8 lanes per 128-element block; U
+    // 64-lane chunks per iteration, all loaded before any is used, with
     // loads clamped to the row (never conditional) so they stay in flight
     // together
     constexpr int EB = MODE == 1 ? 32 : 64;    // source bytes per lane chunk
-    constexpr int U = 2;
     const int nc16 = H / 16;
     const int nblk = H / kFp8Block;
     const unsigned char* src = x + (size_t)t * H * esize;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void fixture_kernel(
 
 // ------------------------------------------------------------------ launchers
 
-template <int KMAX>
+template <int KMAX, int U>
 static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
                               const unsigned char* x, int esize, int T, int H,
                               const int32_t* idx, int k, int E,
@@ -266,15 +266,15 @@ static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
                               int32_t* row_src, int32_t* tok_row, int tblocks,
                               int hs) {
   if (mode == 0)
-    hipLaunchKernelGGL((dispatch_kernel<KMAX, 0>), grid, dim3(256), 0, s, x,
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 0, U>), grid, dim3(256), 0, s, x,
                        esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
                        cap, sc, row_src, tok_row, tblocks, hs);
   else if (mode == 1)
-    hipLaunchKernelGGL((dispatch_kernel<KMAX, 1>), grid, dim3(256), 0, s, x,
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 1, U>), grid, dim3(256), 0, s, x,
                        esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
                        cap, sc, row_src, tok_row, tblocks, hs);
   else
-    hipLaunchKernelGGL((dispatch_kernel<KMAX, 2>), grid, dim3(256), 0, s, x,
+    hipLaunchKernelGGL((dispatch_kernel<KMAX, 2, U>), grid, dim3(256), 0, s, x,
                        esize, T, H, idx, k, E, counts, offsets, tb, sr, rows,
                        cap, sc, row_src, tok_row, tblocks, hs);
 }
@@ -291,8 +291,11 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
   const int esize = xdt == DT_F32 ? 4 : 2;
   const int mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
   // waves per token: about 2048 waves in flight for few tokens, at most one
-  // per group of 64-lane chunks of the row
-  const int groups = mode == 0 ? (H * esize / 16 + 127) / 128 : (H / 16 + 127) / 128;
+  // per group of U 64-lane chunks of the row; U = 1 when groups of two
+  // chunks would leave fewer than 2048 waves
+  const int nch = mode == 0 ? H * esize / 16 : H / 16;   // lane chunks per row
+  const int u = (long long)T * ((nch + 127) / 128) >= 2048 ? 2 : 1;
+  const int groups = (nch + 64 * u - 1) / (64 * u);
   int hs = (2048 + T - 1) / (T > 0 ? T : 1);
   hs = hs < groups ? hs : groups;
   hs = hs < 1 ? 1 : hs;
@@ -302,9 +305,16 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
   unsigned char* rb = (unsigned char*)rows;
   const long long cap = (long long)capacity;
 #define MOE_DISPATCH_K(KV)                                                   \
-  launch_dispatch_k<KV>(mode, grid, s, xb, esize, T, H, topk_idx, k, E,      \
-                        counts, offsets, tb, sr, rb, cap, row_scales,        \
-                        row_src, tok_row, tblocks, hs)
+  do {                                                                       \
+    if (u == 2)                                                              \
+      launch_dispatch_k<KV, 2>(mode, grid, s, xb, esize, T, H, topk_idx, k,  \
+                               E, counts, offsets, tb, sr, rb, cap,          \
+                               row_scales, row_src, tok_row, tblocks, hs);   \
+    else                                                                     \
+      launch_dispatch_k<KV, 1>(mode, grid, s, xb, esize, T, H, topk_idx, k,  \
+                               E, counts, offsets, tb, sr, rb, cap,          \
+                               row_scales, row_src, tok_row, tblocks, hs);   \
+  } while (0)
   if (k <= 1) MOE_DISPATCH_K(1);
   else if (k <= 2) MOE_DISPATCH_K(2);
   else if (k <= 4) MOE_DISPATCH_K(4);
