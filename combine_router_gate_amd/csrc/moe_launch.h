@@ -39,11 +39,10 @@ inline size_t ws_tile_bytes(int T, int E) {
 inline size_t ws_rank_bytes(int T, int k) {
   return align256(size_t(T) * size_t(k) * 4);
 }
-// The partial region ends with 256 bytes holding the completion counter of
-// the small-batch reduction (zeroed by the partial kernel of every call).
+// fp32 partial gate logits of up to split_max(T) hidden ranges
 inline size_t ws_partial_bytes(int T, int E) {
   const int s = split_max(T);
-  return s > 1 ? align256(size_t(s) * T * 64 * gate_epw(E) * 4) + 256 : 0;
+  return s > 1 ? align256(size_t(s) * T * 64 * gate_epw(E) * 4) : 0;
 }
 // Up to this many tokens, histogram, scan and ranks run in one workgroup.
 constexpr int kSmallPlanT = 512;

@@ -19,8 +19,8 @@
 //    about 256 workgroups run; gate_partial_lds_kernel (4096 tokens and
 //    more: 128 tokens x all experts per workgroup, both operands staged
 //    through LDS) or gate_partial_kernel writes the partial logits, and
-//    gate_reduce_quad_kernel (gate_reduce_plan_small_kernel up to 512
-//    tokens) sums them in range order and selects the top-k.  Where a split
+//    gate_reduce_quad_kernel (gate_reduce_small_kernel up to 512 tokens)
+//    sums them in range order and selects the top-k.  Where a split
 //    would not pay, gate_topk_v2_kernel does all of it in one pass.  x is
 //    read with ordinary (allocating) loads, so the dispatch that reads it
 //    next finds much of it still in the memory-attached cache.
@@ -472,20 +472,18 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 
 // Partial logits over one range of the hidden dimension, for shapes where
 // one workgroup per 64-token tile cannot fill the chip (few tokens): the
-// grid is (token tiles of 16*TT, hidden ranges of KR), each workgroup runs
-// the same pipeline as gate_topk_v2_kernel over [k_lo, k_lo + KR) and
-// writes its fp32 partial logits partial[ks][t][e] (row stride 64*EPW).
-// gate_reduce_quad_kernel adds the ranges in ascending order.
+// grid is (token tiles of 16*TT, hidden ranges of KR, expert groups of
+// 64*EPW), each workgroup runs the same pipeline as gate_topk_v2_kernel
+// over [k_lo, k_lo + KR) and writes its fp32 partial logits
+// partial[ks][t][e] (row stride eps >= 64*EPW*gridDim.z).
+// gate_reduce_quad_kernel / gate_reduce_small_kernel add the ranges in
+// ascending order.  Expert groups let few tokens spread over many
+// workgroups with fewer hidden ranges (fewer partial logits to add).
 template <int EPW, int TT, int PQ, int D, int DX = D>
 __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, float* __restrict__ partial,
-    unsigned* __restrict__ done) {
-  // the completion counter of the reduction launched next on this stream
-  if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 &&
-      threadIdx.x == 0)
-    *done = 0u;
-  constexpr int EP = 64 * EPW;             // padded experts
+    int H, int E, int KR, int eps, float* __restrict__ partial) {
+  const int e0 = blockIdx.z * 64 * EPW;    // first expert of the group
   constexpr int TTOK = 16 * TT;            // tokens of the workgroup
   constexpr int KS = 32 * PQ;              // k per super-step
   constexpr int RB = 2 * KS;               // bytes of one x row per step
@@ -520,7 +518,7 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
   const uint16_t* wrow[EPW];
 #pragma unroll
   for (int et = 0; et < EPW; ++et) {
-    const int e = (wv * EPW + et) * 16 + c16;
+    const int e = e0 + (wv * EPW + et) * 16 + c16;
     wrow[et] = w + (size_t)(e < E ? e : E - 1) * H;
   }
 
@@ -569,7 +567,10 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
              ok ? xreg[jx][m] : z);
       }
       lds_barrier();
-      load_x(i + DX, xreg[jx]);
+      // no prefetch past the range: with few steps per range (few tokens,
+      // fine hidden split) those loads would double the traffic; steps past
+      // the range still run (zero x) on the registers' stale finite weights
+      if (i + DX < nss) load_x(i + DX, xreg[jx]);
 #pragma unroll
       for (int q = 0; q < PQ; ++q) {
 #pragma unroll
@@ -586,19 +587,19 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
           }
         }
       }
-      load_w(i + D, wreg[j]);
+      if (i + D < nss) load_w(i + D, wreg[j]);
     }
   }
-  float* out = partial + (size_t)ks * T * EP;
+  float* out = partial + (size_t)ks * T * eps;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int et = 0; et < EPW; ++et) {
-      const int e = (wv * EPW + et) * 16 + c16;
+      const int e = e0 + (wv * EPW + et) * 16 + c16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + tt * 16 + g * 4 + i;
-        if (t < T) out[(size_t)t * EP + e] = acc[tt][et][i];
+        if (t < T) out[(size_t)t * eps + e] = acc[tt][et][i];
       }
     }
 }
@@ -619,9 +620,7 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
 template <int EPW, int TT>
 __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, int tiles, int xg, float* __restrict__ partial,
-    unsigned* __restrict__ done) {
-  if (done != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *done = 0u;
+    int H, int E, int KR, int tiles, int xg, float* __restrict__ partial) {
   // One-dimensional grid of tiles * S workgroups; workgroup i runs on XCD
   // i % 8.  With xg = 8 / S (S dividing 8, tiles a multiple of xg) every XCD
   // serves one hidden range, so its L2 holds 1/S of the gate weight;
@@ -1138,27 +1137,17 @@ __device__ __forceinline__ unsigned long long max64_u64(unsigned long long v) {
 // 4 consecutive experts (16-byte loads across the whole logit row); the
 // token's first wave adds its WPT wave sums in wave order (fixed order: the
 // logits do not depend on timing) and selects the top-k with all 64 lanes
-// (same 64-bit keys and tie-break as topk_select_write).  Each workgroup
-// then publishes its results (device-scope release) and counts itself done;
-// the last one acquires and builds the plan of all tokens.  The counter is
-// zeroed by gate_partial_kernel, which precedes this kernel on the stream.
+// (same 64-bit keys and tie-break as topk_select_write).  The plan follows
+// as plan_small_kernel: a separate launch costs less than having the last
+// workgroup plan after device-scope release/acquire fences in every one.
 template <int C4, int TPW>
-__global__ __launch_bounds__(512) void gate_reduce_plan_small_kernel(
+__global__ __launch_bounds__(512) void gate_reduce_small_kernel(
     const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
-    int pad, const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ logits_dbg,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank,
-    unsigned* __restrict__ done) {
-  constexpr int RW = 8, NT = 64 * RW, B = 8;    // waves, threads, ranges in flight
+    const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ logits_dbg) {
+  constexpr int RW = 8, B = 8;                  // waves, ranges in flight
   constexpr int WPT = RW / TPW;                 // waves per token
-  constexpr int RED = RW * 64 * C4 * 4;         // floats of wave sums
-  constexpr int BITS = (kSmallPlanT / 64) * MOE_MAX_EXPERTS;
-  constexpr int LDS64 = RED / 2 > BITS ? RED / 2 : BITS;
-  __shared__ unsigned long long lds[LDS64];
-  __shared__ int ecnt[MOE_MAX_EXPERTS];
-  __shared__ int last;
-  f32x4* red = (f32x4*)lds;
+  __shared__ f32x4 red[RW * 64 * C4];           // wave sums
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int tk = wv / WPT, part = wv - tk * WPT;
@@ -1242,28 +1231,17 @@ __global__ __launch_bounds__(512) void gate_reduce_plan_small_kernel(
         topk_w[(size_t)t * k + j] = ex[j] / den;
       }
   }
-  // release this workgroup's top-k, count it done; the last one acquires
-  // every other workgroup's results before planning
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  small_plan<NT>(topk_idx, T, k, E, pad, counts, offsets, tile_base,
-                 slot_rank, lds, ecnt);
 }
 
 // ------------------------------------------------------------------ launchers
 
 // What remains of moe_route after the gate kernels.
-enum { kRouteNeedPlan = 0, kRouteNeedScan = 1, kRouteDone = 2 };
+enum { kRouteNeedPlan = 0, kRouteNeedScan = 1 };
 
 template <typename XT>
 static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
-                                    int T, int H, int E, int k, int pad,
+                                    int T, int H, int E, int k,
                                     int32_t* idx, float* tw, float* dbg,
-                                    int32_t* counts, int32_t* offsets,
                                     int32_t* tb, int32_t* sr, int* stage,
                                     hipStream_t s) {
   *stage = kRouteNeedPlan;
@@ -1285,8 +1263,11 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   if constexpr (sizeof(XT) == 2) {
     const int epw = gate_epw(E);
     // Split the hidden dimension so the partial GEMM runs about 256
-    // workgroups (128 for few tokens, whose reduction is the bottleneck);
-    // with a full chip that beats the fused single pass even at 16K tokens.
+    // workgroups (128 below 2048 tokens, whose reduction is the
+    // bottleneck); with a full chip that beats the fused single pass even
+    // at 16K tokens.  Up to kSmallPlanT tokens each workgroup takes one
+    // group of 64 experts, and about 224 workgroups run: less gate weight
+    // per workgroup and fewer hidden ranges to add.
     // From 4096 tokens the LDS-staged kernel takes 128-token tiles with
     // coalesced loads of both operands; it needs hidden ranges of whole
     // 128-element block pairs and 32-bit byte offsets.  Otherwise
@@ -1301,26 +1282,23 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     const int TT = lds_gate ? (T >= 16384 ? 8 : 4)
                    : (epw <= 4 && T >= 8192) ? 8 : T >= 2048 ? 4 : 2;
     const int tiles = (T + 16 * TT - 1) / (16 * TT);
-    const int target = T >= 2048 ? 256 : 128;
+    const bool small = T <= kSmallPlanT;
+    const int eg = small ? epw : 1;        // expert groups
+    const int target = small ? 224 : T >= 2048 ? 256 : 128;
     const int kq = lds_gate ? 128 : 64;    // range granularity
-    int S = (target + tiles - 1) / tiles;
+    int S = (target + tiles * eg - 1) / (tiles * eg);
     S = min(S, min(split_max(T), (H + kq - 1) / kq));
     if (S > 1) {
       const int KR = ((H + S - 1) / S + kq - 1) / kq * kq;
       S = (H + KR - 1) / KR;
       float* part = (float*)((unsigned char*)sr + ws_rank_bytes(T, k));
-      const bool small = T <= kSmallPlanT;
-      unsigned* done =
-          small ? (unsigned*)((unsigned char*)part + ws_partial_bytes(T, E) -
-                              256)
-                : nullptr;
-      const dim3 pgrid(tiles, S);
+      const dim3 pgrid(tiles, S, eg);
 #define MOE_GATE_PART(EPWV, TTV, DV)                                           \
   hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV>), pgrid,          \
-                     dim3(256), 0, s, x, w, T, H, E, KR, part, done)
+                     dim3(256), 0, s, x, w, T, H, E, KR, 64 * EPWV, part)
 #define MOE_GATE_PART_X(EPWV, TTV, DV, DXV)                                    \
   hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV, DXV>), pgrid,     \
-                     dim3(256), 0, s, x, w, T, H, E, KR, part, done)
+                     dim3(256), 0, s, x, w, T, H, E, KR, 64 * EPWV, part)
 #define MOE_GATE_PART_E(TTV)                                                   \
   do {                                                                         \
     if (epw == 1) MOE_GATE_PART(1, TTV, 4);                                    \
@@ -1332,14 +1310,17 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       const int xg = (8 % S == 0 && tiles % (8 / S) == 0) ? 8 / S : 0;
 #define MOE_GATE_LDS_T(EPWV, TTV)                                              \
   hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, TTV>), dim3(tiles * S),   \
-                     dim3(512), 0, s, x, w, T, H, E, KR, tiles, xg, part,     \
-                     done)
+                     dim3(512), 0, s, x, w, T, H, E, KR, tiles, xg, part)
 #define MOE_GATE_LDS(EPWV)                                                     \
   do {                                                                         \
     if (TT == 8) MOE_GATE_LDS_T(EPWV, 4);                                      \
     else MOE_GATE_LDS_T(EPWV, 2);                                              \
   } while (0)
-      if (lds_gate) {
+      if (small) {
+        // TT == 2 below 2048 tokens
+        hipLaunchKernelGGL((gate_partial_kernel<1, 2, 2, 2>), pgrid,
+                           dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw, part);
+      } else if (lds_gate) {
         if (epw == 1) MOE_GATE_LDS(1);
         else if (epw == 2) MOE_GATE_LDS(2);
         else if (epw == 4) MOE_GATE_LDS(4);
@@ -1362,20 +1343,18 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       if (err != hipSuccess) return err;
       const int EPS = 64 * epw;
       if (small) {
-        // one kernel: reduction, top-k, and in its last workgroup the
-        // histogram, scan and ranks of all tokens
-        // 4 tokens per workgroup keeps the completion count (one atomic per
-        // workgroup on one counter) at T / 4
-        const dim3 rgrid((T + 3) / 4);
+        // reduction and top-k with one token per workgroup (its 8 waves
+        // share the ranges), then plan_small_kernel
+        const dim3 rgrid(T);
         if (epw <= 4)
-          hipLaunchKernelGGL((gate_reduce_plan_small_kernel<1, 4>), rgrid,
-                             dim3(512), 0, s, part, S, EPS, T, E, k, pad, bias,
-                             idx, tw, dbg, counts, offsets, tb, sr, done);
+          hipLaunchKernelGGL((gate_reduce_small_kernel<1, 1>), rgrid,
+                             dim3(512), 0, s, part, S, EPS, T, E, k, bias,
+                             idx, tw, dbg);
         else
-          hipLaunchKernelGGL((gate_reduce_plan_small_kernel<2, 4>), rgrid,
-                             dim3(512), 0, s, part, S, EPS, T, E, k, pad, bias,
-                             idx, tw, dbg, counts, offsets, tb, sr, done);
-        *stage = kRouteDone;
+          hipLaunchKernelGGL((gate_reduce_small_kernel<2, 1>), rgrid,
+                             dim3(512), 0, s, part, S, EPS, T, E, k, bias,
+                             idx, tw, dbg);
+        *stage = kRouteNeedPlan;
         return hipGetLastError();
       }
       // reduction: 64-token workgroups that also build the tile histogram
@@ -1467,16 +1446,14 @@ hipError_t launch_route(const void* x, const void* w, int xdt,
   hipError_t err;
   if (xdt == DT_BF16)
     err = launch_gate_typed<uint16_t>((const uint16_t*)x, (const uint16_t*)w,
-                                      bias, T, H, E, k, pad, topk_idx, topk_w,
-                                      logits_dbg, counts, offsets, tile_base,
-                                      slot_rank, &stage, s);
+                                      bias, T, H, E, k, topk_idx, topk_w,
+                                      logits_dbg, tile_base, slot_rank, &stage,
+                                      s);
   else
     err = launch_gate_typed<float>((const float*)x, (const float*)w, bias, T,
-                                   H, E, k, pad, topk_idx, topk_w, logits_dbg,
-                                   counts, offsets, tile_base, slot_rank,
-                                   &stage, s);
+                                   H, E, k, topk_idx, topk_w, logits_dbg,
+                                   tile_base, slot_rank, &stage, s);
   if (err != hipSuccess) return err;
-  if (stage == kRouteDone) return hipSuccess;
   if (stage == kRouteNeedPlan)
     return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
   return launch_scan(tile_base, num_tiles(T), E, pad, counts, offsets, s);

@@ -5,9 +5,9 @@ The library issues no memset and allocates nothing, so one layer's launches
 can be captured once and replayed.  The graph is replayed several times with
 eager work and synchronisations in between, and every replay must equal the
 eager result bit for bit (the kernels are deterministic).  Shapes cover the
-one-kernel small-batch route (its completion counter is reset by a kernel
-on every replay), the split gate with a separate plan, and the fused-
-histogram prefill path with fp8 dispatch.
+small-batch route (split gate, one-token reduction, one-workgroup plan),
+the split gate with a separate histogram and scan, and the fused-histogram
+prefill path with fp8 dispatch.
 """
 import numpy as np
 import pytest
