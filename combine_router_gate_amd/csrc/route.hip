@@ -1198,38 +1198,45 @@ __global__ __launch_bounds__(512) void gate_reduce_small_kernel(
                             : 0ull;
       }
     }
-    int sel_e[MOE_MAX_TOPK];
-    float sel_v[MOE_MAX_TOPK];
+    // this lane's keys in descending order (odd-even transposition), so a
+    // round's candidate is key[0] and the winning lane shifts its list
+    constexpr int NK = C4 * 4;
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      sel_e[j] = 0;
-      sel_v[j] = 0.0f;
-      if (j < k) {
-        unsigned long long best = key[0];
+    for (int r = 0; r < NK; ++r)
 #pragma unroll
-        for (int i = 1; i < C4 * 4; ++i) best = key[i] > best ? key[i] : best;
-        best = max64_u64(best);
-        const uint32_t blo = (uint32_t)best;
-#pragma unroll
-        for (int i = 0; i < C4 * 4; ++i)
-          if ((uint32_t)key[i] == blo) key[i] &= 0xffffffffull;
-        sel_e[j] = (int)(0xffffffffu - blo);
-        sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
+      for (int i = r & 1; i + 1 < NK; i += 2) {
+        const unsigned long long hi = key[i] > key[i + 1] ? key[i] : key[i + 1];
+        const unsigned long long lo = key[i] > key[i + 1] ? key[i + 1] : key[i];
+        key[i] = hi;
+        key[i + 1] = lo;
       }
+    // k rounds of a 64-lane max; lane j keeps the j-th choice
+    int my_e = 0;
+    uint32_t my_key = 0u, top_key = 0u;
+    for (int j = 0; j < k; ++j) {
+      const unsigned long long best = max64_u64(key[0]);
+      const uint32_t blo = (uint32_t)best;
+      const bool win = (uint32_t)key[0] == blo;
+#pragma unroll
+      for (int i = 0; i + 1 < NK; ++i) key[i] = win ? key[i + 1] : key[i];
+      key[NK - 1] = win ? 0ull : key[NK - 1];
+      if (lane == j) {
+        my_e = (int)(0xffffffffu - blo);
+        my_key = (uint32_t)(best >> 32);
+      }
+      if (j == 0) top_key = (uint32_t)(best >> 32);
     }
-    float ex[MOE_MAX_TOPK];
+    // weights exp(l_j - l_0) / sum over the chosen, the sum in choice order
+    const float ex = lane < k ? expf(f32_from_order_key(my_key) -
+                                     f32_from_order_key(top_key))
+                              : 0.0f;
     float den = 0.0f;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      ex[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.0f;
-      den += ex[j];
+    for (int j = 0; j < k; ++j)
+      den += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ex), j));
+    if (lane < k) {
+      topk_idx[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = ex / den;
     }
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k && lane == j) {
-        topk_idx[(size_t)t * k + j] = sel_e[j];
-        topk_w[(size_t)t * k + j] = ex[j] / den;
-      }
   }
 }
 
