@@ -18,7 +18,8 @@
 //  * E >= 64, bf16: the hidden dimension is split into S ranges so that
 //    about 256 workgroups run; gate_partial_lds_kernel (4096 tokens and
 //    more: 128 tokens x all experts per workgroup, both operands staged
-//    through LDS) or gate_partial_kernel writes the partial logits, and
+//    through LDS) or gate_partial_kernel (up to 512 tokens with one group
+//    of 64 experts per workgroup) writes the partial logits, and
 //    gate_reduce_quad_kernel (gate_reduce_small_kernel up to 512 tokens)
 //    sums them in range order and selects the top-k.  Where a split
 //    would not pay, gate_topk_v2_kernel does all of it in one pass.  x is
