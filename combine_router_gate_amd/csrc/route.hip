@@ -1271,11 +1271,14 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   if constexpr (sizeof(XT) == 2) {
     const int epw = gate_epw(E);
     // Split the hidden dimension so the partial GEMM runs about 256
-    // workgroups (128 below 2048 tokens, whose reduction is the
-    // bottleneck); with a full chip that beats the fused single pass even
-    // at 16K tokens.  Up to kSmallPlanT tokens each workgroup takes one
-    // group of 64 experts, and about 224 workgroups run: less gate weight
-    // per workgroup and fewer hidden ranges to add.
+    // workgroups; with a full chip that beats the fused single pass even
+    // at 16K tokens.  Below 4096 tokens (gate_partial_kernel) workgroups
+    // also split the experts: up to kSmallPlanT tokens 32-token tiles and
+    // one group of 64 experts per workgroup, ~224 workgroups; above that
+    // 64-token tiles, 64 experts per workgroup up to 2048 tokens and 128
+    // beyond, 4 or 8 hidden ranges (8 while that stays within ~800
+    // workgroups).  Less gate weight per workgroup and fewer ranges to add
+    // measured 1.2-2.3x faster than whole expert rows per workgroup.
     // From 4096 tokens the LDS-staged kernel takes 128-token tiles with
     // coalesced loads of both operands; it needs hidden ranges of whole
     // 128-element block pairs and 32-bit byte offsets.  Otherwise
@@ -1287,14 +1290,23 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
                           (size_t)E * H * 2 <= 0xffffffffu;
     // LDS-staged gate: 128-token tiles from 16384 tokens, 64-token tiles
     // below (more workgroups for a smaller hidden split, so fewer partials)
-    const int TT = lds_gate ? (T >= 16384 ? 8 : 4)
-                   : (epw <= 4 && T >= 8192) ? 8 : T >= 2048 ? 4 : 2;
-    const int tiles = (T + 16 * TT - 1) / (16 * TT);
     const bool small = T <= kSmallPlanT;
-    const int eg = small ? epw : 1;        // expert groups
-    const int target = small ? 224 : T >= 2048 ? 256 : 128;
+    const bool mid = !lds_gate && !small && T < 4096;
+    const int TT = lds_gate ? (T >= 16384 ? 8 : 4)
+                   : small ? 2 : mid ? 4
+                   : (epw <= 4 && T >= 8192) ? 8 : 4;
+    const int tiles = (T + 16 * TT - 1) / (16 * TT);
+    // 64-expert tiles per workgroup, and expert groups
+    const int epg = (mid && T > 2048 && epw % 2 == 0) ? 2 : 1;
+    const int eg = (small || mid) ? epw / epg : 1;
     const int kq = lds_gate ? 128 : 64;    // range granularity
-    int S = (target + tiles * eg - 1) / (tiles * eg);
+    int S;
+    if (mid) {
+      S = tiles * eg * 8 <= 800 ? 8 : 4;
+    } else {
+      const int target = small ? 224 : 256;
+      S = (target + tiles * eg - 1) / (tiles * eg);
+    }
     S = min(S, min(split_max(T), (H + kq - 1) / kq));
     if (S > 1) {
       const int KR = ((H + S - 1) / S + kq - 1) / kq * kq;
@@ -1325,9 +1337,17 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     else MOE_GATE_LDS_T(EPWV, 2);                                              \
   } while (0)
       if (small) {
-        // TT == 2 below 2048 tokens
         hipLaunchKernelGGL((gate_partial_kernel<1, 2, 2, 2>), pgrid,
                            dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw, part);
+      } else if (mid) {
+        if (epg == 1)
+          hipLaunchKernelGGL((gate_partial_kernel<1, 4, 2, 2>), pgrid,
+                             dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw,
+                             part);
+        else
+          hipLaunchKernelGGL((gate_partial_kernel<2, 4, 2, 2>), pgrid,
+                             dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw,
+                             part);
       } else if (lds_gate) {
         if (epw == 1) MOE_GATE_LDS(1);
         else if (epw == 2) MOE_GATE_LDS(2);
@@ -1337,10 +1357,8 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
         if (epw == 1) MOE_GATE_PART(1, 8, 3);
         else if (epw == 2) MOE_GATE_PART(2, 8, 3);
         else MOE_GATE_PART_X(4, 8, 2, 4);   // x 4 steps ahead: +5%
-      } else if (TT == 4) {
-        MOE_GATE_PART_E(4);
       } else {
-        MOE_GATE_PART_E(2);
+        MOE_GATE_PART_E(4);
       }
 #undef MOE_GATE_LDS
 #undef MOE_GATE_LDS_T

@@ -64,13 +64,19 @@ SMALL = {
     # few experts (E <= 32) and many bf16 tokens take the LDS-staged gate too
     "lds_gate_t4200_e24": C["mixtral"].with_shape(T=4200, H=512, E=24, k=3,
                                                   pad=16),
-    # the reduction's range chunks (S = 8 in chunks of 4, and of 2 for 24
-    # and 32 expert tiles) and its 16-token workgroups (512 < T < 1024)
+    # 512 < T < 4096: 64-token tiles with expert groups of 64 (128 above
+    # 2048 tokens), 4 or 8 hidden ranges; the reduction's range chunks
+    # (S = 8 in chunks of 4, and of 2 for 24 and 32 expert tiles) and its
+    # 16-token workgroups
     "reduce_t2048_s8": C["dsv3_prefill"].with_shape(T=2048, H=1024),
     "reduce_t2048_e384_s8": C["moonep_skew"].with_shape(T=2048, H=1024),
     "reduce_t1024_e512_s4": C["moonep_skew"].with_shape(T=1024, H=512, E=512,
                                                         zipf_bias=False),
     "reduce_t700_e256": C["dsv3_decode"].with_shape(T=700, H=1024),
+    "reduce_t700_e384_s8": C["moonep_skew"].with_shape(T=700, H=1024),
+    "mid_t2500_e256": C["dsv3_prefill"].with_shape(T=2500, H=1024),
+    "mid_t4095_e100": C["mixtral"].with_shape(T=4095, H=384, E=100, k=4,
+                                              pad=16),
     # the most experts (512) with many tokens: split gate with 64-token
     # tiles, reduction in chunks of two ranges
     "e512_t4096": C["moonep_skew"].with_shape(T=4096, H=256, E=512, k=8,
