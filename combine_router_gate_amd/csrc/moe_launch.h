@@ -18,20 +18,23 @@ inline int num_tiles(int T) { return (T + 63) / 64; }
 //   slot_rank [T, k] int32       rank of slot (t, j) among its tile's tokens
 //                                that chose the same expert
 //   partial   [S, T, EP] fp32    partial gate logits when the hidden
-//                                dimension is split S ways (up to kSplitRows
-//                                tokens); S * T <= 2 * kSplitRows, EP =
+//                                dimension is split S ways (up to
+//                                kSplitMaxT tokens); S <= split_max(T), EP =
 //                                experts padded to the gate's 64 * EPW
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 constexpr int kSplitRows = 16384;
 constexpr int kSplitMax = 64;
+constexpr int kSplitMaxT = 65536;      // more tokens: the one-pass gate
 inline int gate_epw(int E) {           // expert tiles per wave of the gate
   const int et = (E + 15) / 16;
   return et <= 4 ? 1 : et <= 8 ? 2 : et <= 16 ? 4 : et <= 24 ? 6 : 8;
 }
-inline int split_max(int T) {          // largest split of H for T tokens
-  if (T <= 0 || T > 2 * kSplitRows) return 1;
+// Largest split of H for T tokens: 2 * kSplitRows partial rows, at least 4
+// ranges up to kSplitMaxT tokens.
+inline int split_max(int T) {
+  if (T <= 0 || T > kSplitMaxT) return 1;
   const int s = 2 * kSplitRows / T;
-  return s < kSplitMax ? s : kSplitMax;
+  return s < 4 ? 4 : s < kSplitMax ? s : kSplitMax;
 }
 inline size_t ws_tile_bytes(int T, int E) {
   return align256(size_t(num_tiles(T)) * size_t(E) * 4);

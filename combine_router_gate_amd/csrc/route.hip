@@ -1288,11 +1288,11 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
                           (epw <= 4 || epw == 6) &&
                           (size_t)T * H * 2 <= 0xffffffffu &&
                           (size_t)E * H * 2 <= 0xffffffffu;
-    // LDS-staged gate: 128-token tiles from 16384 tokens, 64-token tiles
-    // below (more workgroups for a smaller hidden split, so fewer partials)
+    // LDS-staged gate: 64-token tiles up to 8192 tokens (more workgroups
+    // for a smaller hidden split, so fewer partials), 128-token tiles above
     const bool small = T <= kSmallPlanT;
     const bool mid = !lds_gate && !small && T < 4096;
-    const int TT = lds_gate ? (T >= 16384 ? 8 : 4)
+    const int TT = lds_gate ? (T > 8192 ? 8 : 4)
                    : small ? 2 : mid ? 4
                    : (epw <= 4 && T >= 8192) ? 8 : 4;
     const int tiles = (T + 16 * TT - 1) / (16 * TT);
@@ -1303,6 +1303,16 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
     int S;
     if (mid) {
       S = tiles * eg * 8 <= 800 ? 8 : 4;
+    } else if (lds_gate) {
+      // one workgroup per CU: the split S of 2..4 with the least work per
+      // CU, rounds(S) / S with rounds = ceil(tiles * S / 256), the fewer
+      // ranges on a tie (measured best at 8K-32K tokens; 2 at 16384)
+      S = 2;
+      for (int c = 3; c <= 4; ++c) {
+        const long long rc = ((long long)tiles * c + 255) / 256;
+        const long long rs = ((long long)tiles * S + 255) / 256;
+        if (rc * S < rs * c) S = c;
+      }
     } else {
       const int target = small ? 224 : 256;
       S = (target + tiles * eg - 1) / (tiles * eg);

@@ -100,7 +100,7 @@ size_t moe_rows_capacity(int T, int E, int k, int pad);
 
 /* Bytes of scratch that moe_route / moe_plan write and moe_dispatch reads
  * (per-tile expert counts and prefixes, per-slot ranks, and for up to
- * 16384 tokens room for partial gate logits when the gate splits the hidden
+ * 65536 tokens room for partial gate logits when the gate splits the hidden
  * dimension).  A workspace belongs to one route -> dispatch sequence at
  * a time: calls in flight on different streams need different workspaces.
  * 0 if T == 0. */

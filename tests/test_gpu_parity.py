@@ -83,6 +83,13 @@ SMALL = {
                                               zipf_bias=False),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
+# gate shapes above 8192 tokens (route only: the dispatch and combine of
+# these sizes are the full workloads' paths): 128-token tiles with 3 hidden
+# ranges, and more than 16384 tokens (split gate, fused-histogram reduction)
+ROUTE_ONLY = {
+    "lds_gate_t10000_s3": C["dsv3_prefill"].with_shape(T=10000, H=1024),
+    "lds_gate_t20000": C["dsv3_prefill"].with_shape(T=20000, H=512),
+}
 
 
 def _route_gpu(wl):
@@ -119,6 +126,11 @@ def _route_case(name, cfg, seed):
 @pytest.mark.parametrize("name", list(SMALL))
 def test_route_small(name):
     _route_case(name, SMALL[name], 1)
+
+
+@pytest.mark.parametrize("name", list(ROUTE_ONLY))
+def test_route_large(name):
+    _route_case(name, ROUTE_ONLY[name], 1)
 
 
 @pytest.mark.parametrize("name", FULL)
