@@ -380,8 +380,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dsv3_prefill")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="tokens in the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens in the CPU-oracle baseline sample, at most "
+                    "the workload's (0 = skip)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the backward and FarSkip-overlap measurements "
                     "that follow the timed steps")
@@ -560,7 +561,8 @@ def main():
                 cfg, moe, y, d["tok_row"], p["topk_w"], shared, resid,
                 stream, dev)
     if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_tokens)
+        line["cpu_baseline"] = cpu_baseline(cfg, wl, min(args.cpu_tokens,
+                                                         cfg.T))
     print(json.dumps(line), flush=True)
 
 
