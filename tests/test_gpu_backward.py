@@ -224,3 +224,27 @@ def test_farskip_split_equals_fused(name, with_shared):
 def test_farskip_aux_empty():
     r = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     assert moe.farskip_aux(None, r).shape == (0, 256)
+
+
+@pytest.mark.parametrize("name", ["decode", "mixtral_s"])
+def test_backward_deterministic(name):
+    """Both backward passes give the same bits on every call (fixed
+    summation orders, no atomics)."""
+    cfg = SMALL[name]
+    note(f"backward determinism {name}")
+    wl, o, d, y, o_tok, o_src = _forward(cfg, 13)
+    g = to_dev(I.grad_tensor(13, (cfg.T, cfg.H)))
+    w = to_dev(o["topk_w"])
+    cap = d["rows"].shape[0]
+    G = to_dev(I.grad_tensor(13, (cap, cfg.H), stream=1))
+    first = None
+    for _ in range(3):
+        gy, gw = moe.combine_backward(g, y, d["tok_row"], w)
+        gx = moe.dispatch_backward(G, d["tok_row"])
+        torch.cuda.synchronize()
+        cur = (gy.view(torch.int16).clone(), gw.view(torch.int32).clone(),
+               gx.view(torch.int32).clone())
+        if first is None:
+            first = cur
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(first, cur))

@@ -151,3 +151,26 @@ def test_expert_gemm_prefill_full_size_sampled():
     others = [e for e in range(cfg.E) if e not in pick][::37]
     rs = np.array([int(o["offsets"][e]) for e in others])
     assert not to_host(y[torch.from_numpy(rs).cuda()]).any()
+
+
+def test_expert_gemm_deterministic():
+    """The grouped GEMM gives the same bits on every call."""
+    cfg, N, ydt = next(iter(CASES.values()))
+    note(f"expert gemm determinism T={cfg.T} K={cfg.H} N={N} E={cfg.E}")
+    wl = I.make_workload(cfg, 37)
+    o = O.route(wl.x.values, wl.w_gate.values, wl.bias, cfg.k, cfg.pad)
+    p = moe.plan(to_dev(o["topk_idx"]), cfg.E, cfg.pad)
+    d = moe.dispatch(to_dev(wl.x), p, payload="fp8")
+    w, sw = I.expert_weights_fp8(37, cfg.E, N, cfg.H)
+    w, sw = to_dev(w), to_dev(sw)
+    cap = d["rows"].shape[0]
+    ws = torch.empty(moe.moe_expert_gemm_workspace_bytes(cap, cfg.E),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        y = torch.zeros((cap, N), dtype=torch_dtype(ydt), device="cuda")
+        moe.moe_expert_gemm_fp8(d["rows"], d["row_scales"], d["row_src"],
+                                p["offsets"], w, sw, y, ws)
+        torch.cuda.synchronize()
+        outs.append(y.view(torch.int16 if ydt == "bf16" else torch.int32))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
