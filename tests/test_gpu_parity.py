@@ -89,6 +89,12 @@ FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 ROUTE_ONLY = {
     "lds_gate_t10000_s3": C["dsv3_prefill"].with_shape(T=10000, H=1024),
     "lds_gate_t20000": C["dsv3_prefill"].with_shape(T=20000, H=512),
+    # first shapes past each policy boundary: 513 tokens (64-token tiles
+    # with expert groups), 8193 (128-token tiles), 16321 (64-token
+    # reduction workgroups that build the tile histogram)
+    "mid_t513": C["dsv3_decode"].with_shape(T=513, H=512),
+    "lds_gate_t8193": C["dsv3_prefill"].with_shape(T=8193, H=512),
+    "fused_hist_t16321": C["moonep_skew"].with_shape(T=16321, H=256),
 }
 
 
