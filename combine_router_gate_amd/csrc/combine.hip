@@ -187,10 +187,11 @@ static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                        y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
 }
 
-// Waves per token: enough waves in flight for few tokens (about 2048),
-// never more than the token row has 64*U-chunk groups.
+// Waves per token: up to about 16384 waves in flight (4096 tokens of a
+// 4096-wide row: 22.1 -> 21.2 us), never more than the token row has
+// 64*U-chunk groups.
 static int waves_per_token(int T, int groups_per_row) {
-  const int want = (2048 + T - 1) / T;
+  const int want = (16384 + T - 1) / T;
   const int hs = want < groups_per_row ? want : groups_per_row;
   return hs < 1 ? 1 : hs;
 }
@@ -200,8 +201,8 @@ hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
                           int k, const void* shared, const void* res_in,
                           void* res_out, void* rnr, void* out, int odt,
                           hipStream_t s) {
-  // two groups of 64 chunks per lane step, or one when that leaves too few
-  // waves for the chip (few tokens)
+  // two groups of 64 chunks per lane step, or one when that leaves fewer
+  // than 2048 waves (few tokens)
   const int groups2 = (H / 8 + 127) / 128;
   const int u = (long long)T * groups2 >= 2048 ? 2 : 1;
   const int hs = waves_per_token(T, u == 2 ? groups2 : (H / 8 + 63) / 64);
@@ -370,10 +371,11 @@ hipError_t launch_combine_backward(const void* g, const void* y, int ydt,
                                    const float* topk_w, int T, int k,
                                    void* grad_y, float* grad_w,
                                    hipStream_t s) {
-  // waves per token: a power of two up to 16, enough for ~2048 waves
+  // waves per token: a power of two up to 16, for up to ~16384 waves
+  // (MoonEP 8192 tokens of 768: 42 -> 39.5 us)
   const int groups = (H / 8 + 63) / 64;
   int hs = 1;
-  while (hs < 16 && 2 * hs <= groups && (long long)T * hs < 2048) hs *= 2;
+  while (hs < 16 && 2 * hs <= groups && (long long)T * hs < 16384) hs *= 2;
   const int waves = hs > 4 ? hs : 4;
   const int tpb = waves / hs;
   const dim3 grid((unsigned)((T + tpb - 1) / tpb)), block(64 * waves);
