@@ -11,13 +11,13 @@
 //   residual           = residual + MoE output
 // so the auxiliary stream never depends on the routed combine.
 //
-// Design for CDNA4: one wavefront per token (several per token when there
-// are too few tokens to fill the chip).  Lanes 0..k-1 fetch the k
-// (row, weight) pairs, broadcast to scalar registers; each lane then owns
-// two groups of 8 consecutive hidden elements per step (one when there are
-// few tokens, to spread a row over more waves) and issues all their 16-byte
-// row gathers plus the residual and shared loads before any arithmetic (20
-// independent loads in flight per lane at k = 8),
+// Design for CDNA4: a token's row is split into groups of 128 16-byte
+// chunks (64 with few tokens), one wavefront each, so the waves of a token
+// run side by side.  Lanes 0..k-1 fetch the k (row, weight) pairs,
+// broadcast to scalar registers; each lane then owns two groups of 8
+// consecutive hidden elements (one with few tokens) and issues all their
+// 16-byte row gathers plus the residual and shared loads before any
+// arithmetic (20 independent loads in flight per lane at k = 8),
 // accumulates in fp32 with j ascending (fmaf), adds shared then residual,
 // rounds once to bf16 with the hardware converter and writes with streaming
 // stores.  No floating-point atomics: every output element is produced by
@@ -74,8 +74,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
     unsigned char* __restrict__ rnr, unsigned char* __restrict__ out,
     int hsplit) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // wave -> (token, part): with few tokens, hsplit waves share one token's
-  // hidden dimension (interleaved groups of 64*U chunks)
+  // wave -> (token, part): hsplit waves share one token's hidden dimension
+  // (interleaved groups of 64*U chunks)
   const int gw = blockIdx.x * 4 + wv;
   const int t = gw / hsplit, part = gw - t * hsplit;
   if (t >= T) return;
@@ -187,25 +187,20 @@ static void launch_combine_k(int om, dim3 grid, hipStream_t s,
                        y, y_rows, H, tok_row, w, T, k, sh, ri, ro, rn, out, hs);
 }
 
-// Waves per token: up to about 16384 waves in flight (4096 tokens of a
-// 4096-wide row: 22.1 -> 21.2 us), never more than the token row has
-// 64*U-chunk groups.
-static int waves_per_token(int T, int groups_per_row) {
-  const int want = (16384 + T - 1) / T;
-  const int hs = want < groups_per_row ? want : groups_per_row;
-  return hs < 1 ? 1 : hs;
-}
 
 hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
                           const int32_t* tok_row, const float* topk_w, int T,
                           int k, const void* shared, const void* res_in,
                           void* res_out, void* rnr, void* out, int odt,
                           hipStream_t s) {
-  // two groups of 64 chunks per lane step, or one when that leaves fewer
-  // than 2048 waves (few tokens)
+  // Every group of 64*U chunks of a token row is a wave of its own (the
+  // waves of one token run side by side instead of one wave looping over
+  // the row: DeepSeek-V3 prefill 535 -> 504 us, 7 waves per token); two
+  // 64-lane chunks per lane step, or one when that leaves fewer than 2048
+  // waves (few tokens)
   const int groups2 = (H / 8 + 127) / 128;
   const int u = (long long)T * groups2 >= 2048 ? 2 : 1;
-  const int hs = waves_per_token(T, u == 2 ? groups2 : (H / 8 + 63) / 64);
+  const int hs = u == 2 ? groups2 : (H / 8 + 63) / 64;
   const dim3 grid((unsigned)(((long long)T * hs + 3) / 4));
   const int om = res_in != nullptr ? (rnr != nullptr ? 0 : 3)
                                    : (odt == DT_BF16 ? 1 : 2);

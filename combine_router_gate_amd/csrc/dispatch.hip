@@ -12,9 +12,9 @@
 // + rank of t among the tile's tokens that chose e, i.e. ascending token
 // order inside every expert segment.
 //
-// Design for CDNA4: one wavefront per token (several per token when there
-// are too few tokens to fill the chip, each taking an interleaved share of
-// the row).  Lanes 0..k-1 resolve the k
+// Design for CDNA4: a token's row is split into groups of 64-lane chunks
+// (two chunks per lane, or one with few tokens), one wavefront each, so the
+// waves of a token run side by side.  Lanes 0..k-1 resolve the k
 // destination rows, which are then broadcast to scalar registers; the token
 // row is read from HBM once in 16-byte vectors (coalesced across the wave)
 // and written k times with streaming (non-temporal) stores, which measured
@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
       row_src[r] = -1;
     return;
   }
-  // wave -> (token, part): with few tokens, hsplit waves share one token's
-  // row (interleaved groups of 64-lane chunks); part 0 writes the metadata
+  // wave -> (token, part): hsplit waves share one token's row (interleaved
+  // groups of 64-lane chunks); part 0 writes the metadata
   const int gw = blockIdx.x * 4 + wv;
   const int t = gw / hsplit, part = gw - t * hsplit;
   if (t >= T) return;
@@ -290,15 +290,13 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
       (const int32_t*)((const unsigned char*)workspace + ws_tile_bytes(T, E));
   const int esize = xdt == DT_F32 ? 4 : 2;
   const int mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
-  // waves per token: up to about 16384 waves in flight, at most one per
-  // group of U 64-lane chunks of the row; U = 1 when groups of two chunks
+  // every group of U 64-lane chunks of a token row is a wave of its own
+  // (a token's waves run side by side); U = 1 when groups of two chunks
   // would leave fewer than 16384 waves (Mixtral 4096 tokens: 26 -> 22 us,
   // MoonEP 8192 tokens of 768: 26.4 -> 24.5 us)
   const int nch = mode == 0 ? H * esize / 16 : H / 16;   // lane chunks per row
   const int u = (long long)T * ((nch + 127) / 128) >= 16384 ? 2 : 1;
-  const int groups = (nch + 64 * u - 1) / (64 * u);
-  int hs = (16384 + T - 1) / (T > 0 ? T : 1);
-  hs = hs < groups ? hs : groups;
+  int hs = (nch + 64 * u - 1) / (64 * u);
   hs = hs < 1 ? 1 : hs;
   const int tblocks = (int)(((long long)T * hs + 3) / 4);
   const dim3 grid(tblocks + kDispatchFillBlocks);
