@@ -260,9 +260,11 @@ __global__ __launch_bounds__(256) void farskip_aux_kernel(
 
 hipError_t launch_farskip_aux(const void* shared, const void* residual,
                               void* rnr, int T, int H, hipStream_t s) {
+  // one 16-byte vector per thread (a grid-stride loop of 4096 workgroups
+  // measured 125 us at DeepSeek-V3 prefill, this 111 us)
   const long long n16 = (long long)T * H / 8;
   long long blocks = (n16 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 0x7fffffffLL) blocks = 0x7fffffffLL;
   hipLaunchKernelGGL(farskip_aux_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      s, (const unsigned char*)shared,
                      (const unsigned char*)residual, (unsigned char*)rnr, n16);
