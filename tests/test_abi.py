@@ -71,6 +71,14 @@ def test_workspace_bytes(L):
     w = moe.moe_workspace_bytes(16384, 256, 8)
     assert w >= 4 * (256 * 256 + 16384 * 8)
     assert moe.moe_workspace_bytes(65, 8, 2) >= 4 * (2 * 8 + 65 * 2)
+    # room for the split gate's partial logits: up to 4 hidden ranges of
+    # fp32 [T, 64 * ceil(E / 64)] through 65536 tokens, none beyond
+    for T, E in ((20000, 256), (65536, 512), (4096, 384)):
+        tiles = 4 * ((T + 63) // 64) * E + 4 * T * 8
+        assert moe.moe_workspace_bytes(T, E, 8) >= tiles + 4 * 4 * T * 64 * (
+            (E + 63) // 64)
+    T = 65537
+    assert moe.moe_workspace_bytes(T, 256, 8) < 2 * 4 * T * 256
 
 
 # fake, 256-aligned, far-apart device addresses (never dereferenced)
