@@ -104,3 +104,63 @@ def check_f32_close(gpu, exact64, what=""):
     o = np.asarray(exact64, dtype=np.float64)
     bad = np.abs(g - o) > 1e-5 * np.abs(o) + 1e-6
     assert not bad.any(), (what, np.abs(g - o).max(), np.argwhere(bad)[:5])
+
+
+def order_keys(logits_f32) -> np.ndarray:
+    """Order-preserving integer key of float32 values (larger value, larger
+    key; -0 ranks just below +0), as int64."""
+    u = np.ascontiguousarray(logits_f32, dtype=np.float32).view(
+        np.uint32).astype(np.int64)
+    neg = (u & 0x80000000) != 0
+    return np.where(neg, (~u) & 0xFFFFFFFF, u | 0x80000000)
+
+
+def check_topk_own_logits(gpu_idx, gpu_w, gpu_logits, k):
+    """The GPU's top-k must be exactly the first k experts of its own fp32
+    logits ranked by (logit descending, expert index ascending), in that
+    order, on every token; its weights within fp32 rounding of the softmax
+    over those k logits.  A test-side check of the selection alone: it
+    involves no oracle and needs no tolerance on the indices."""
+    key = order_keys(gpu_logits)
+    order = np.argsort(-key, axis=1, kind="stable")[:, :k]
+    gi = np.asarray(gpu_idx)
+    bad = np.nonzero((order != gi).any(axis=1))[0]
+    assert bad.size == 0, ("top-k differs from the GPU's own logits at tokens",
+                           bad[:10], gi[bad[:3]], order[bad[:3]])
+    sel = np.take_along_axis(np.asarray(gpu_logits, dtype=np.float64), order,
+                             axis=1)
+    ex = np.exp(sel - sel[:, :1])
+    w = ex / ex.sum(axis=1, keepdims=True)
+    err = np.abs(np.asarray(gpu_w, dtype=np.float64) - w)
+    assert err.max() <= 2e-6, ("weights vs own logits", err.max())
+
+
+def check_plan_valid(topk_idx, counts, offsets, tok_row, row_src, E, pad):
+    """Everything a routing plan must satisfy for the given top-k choice;
+    together these fix counts, offsets, tok_row and row_src uniquely:
+    counts are the per-expert histogram, offsets the exclusive scan of the
+    counts rounded up to pad, expert e's tokens fill [offsets[e],
+    offsets[e] + counts[e]) in ascending token order, row_src inverts
+    tok_row and every other row is -1."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = idx.shape
+    cnt = np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(np.asarray(counts), cnt)
+    seg = -(-cnt // pad) * pad
+    assert np.array_equal(np.asarray(offsets, dtype=np.int64),
+                          np.concatenate([[0], np.cumsum(seg)]))
+    tr = np.asarray(tok_row, dtype=np.int64)
+    rs = np.asarray(row_src, dtype=np.int64)
+    # ascending token order inside each segment (slot order within a token
+    # is irrelevant: a token picks an expert at most once)
+    tok = np.repeat(np.arange(T), k)
+    ex = idx.ravel()
+    ordr = np.lexsort((tok, ex))
+    expect = np.empty(T * k, dtype=np.int64)
+    first = np.asarray(offsets, dtype=np.int64)[ex[ordr]]
+    rank = np.arange(T * k) - np.concatenate([[0], np.cumsum(cnt)])[ex[ordr]]
+    expect[ordr] = first + rank
+    assert np.array_equal(tr.ravel(), expect), "tok_row"
+    want_src = np.full(rs.shape[0], -1, dtype=np.int64)
+    want_src[expect] = tok
+    assert np.array_equal(rs, want_src), "row_src"

@@ -17,7 +17,8 @@ import torch
 from combine_router_gate_amd import inputs as I
 from combine_router_gate_amd import moe
 from oracle import moe_oracle as O
-from _gpu_common import (LOGIT_TOL, check_bf16_close, check_f32_close, note,
+from _gpu_common import (LOGIT_TOL, check_bf16_close, check_f32_close,
+                         check_plan_valid, check_topk_own_logits, note,
                          to_dev, to_host, topk_audit, torch_dtype)
 
 pytestmark = pytest.mark.gpu
@@ -105,28 +106,49 @@ def _route_gpu(wl):
     return moe.route(x, w, cfg.k, cfg.pad, bias=b, want_logits=True), x
 
 
-def _route_case(name, cfg, seed):
+def _route_case(name, cfg, seed, sample_rows=64):
+    """Route on the GPU, compare with the oracle, then dispatch from the
+    route's own workspace (the plan the benchmark runs) and check the rows
+    it produced."""
     note(f"route {name} seed={seed} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
     wl = I.make_workload(cfg, seed)
-    p, _ = _route_gpu(wl)
+    p, x = _route_gpu(wl)
+    d = moe.dispatch(x, p, payload="fp8" if cfg.payload == "fp8" else "same")
     torch.cuda.synchronize()
     o = O.route(wl.x.values, wl.w_gate.values, wl.bias, cfg.k, cfg.pad)
     gl = to_host(p["logits"])
     dl = np.abs(gl.astype(np.float64) - o["logits"]).max()
     assert dl <= LOGIT_TOL, dl
     gi, gw = to_host(p["topk_idx"]), to_host(p["topk_w"])
+    check_topk_own_logits(gi, gw, gl, cfg.k)
     near = topk_audit(gi, gw, o["logits"], gl, cfg.k)
     counts, offs = to_host(p["counts"]), to_host(p["offsets"])
-    if (gi == o["topk_idx"]).all():
+    tok_row, row_src = to_host(d["tok_row"]), to_host(d["row_src"])
+    same = bool((gi == o["topk_idx"]).all())
+    if same:
+        cap = O.rows_capacity(cfg.T, cfg.E, cfg.k, cfg.pad)
+        o_tok, o_src = O.assign_slots(o["topk_idx"], o["offsets"], cfg.E, cap)
         assert np.array_equal(counts, o["counts"])
         assert np.array_equal(offs, o["offsets"])
-    else:   # a near tie went the other way: the plan must still be valid
-        assert counts.sum() == cfg.T * cfg.k
-        assert np.array_equal(counts, np.bincount(gi.ravel(), minlength=cfg.E))
-        seg = np.diff(offs.astype(np.int64))
-        assert offs[0] == 0 and (seg % cfg.pad == 0).all()
-        assert ((seg >= counts) & (seg - counts < cfg.pad)).all()
-    note(f"route {name}: max|dlogit|={dl:.2e} near-ties={near}")
+        assert np.array_equal(tok_row, o_tok)
+        assert np.array_equal(row_src, o_src)
+    else:   # a near tie went the other way: the plan must still be exact
+        # for the GPU's own choice
+        check_plan_valid(gi, counts, offs, tok_row, row_src, cfg.E, cfg.pad)
+    # sampled rows of the payload (row_src verified above)
+    valid = np.nonzero(row_src >= 0)[0]
+    rsel = np.random.default_rng(seed).choice(
+        valid, min(sample_rows, len(valid)), replace=False)
+    ridx = torch.from_numpy(rsel.astype(np.int64)).cuda()
+    g_rows = to_host(d["rows"][ridx])
+    g_sc = to_host(d["row_scales"][ridx]) if cfg.payload == "fp8" else None
+    for i, r in enumerate(rsel):
+        pay, sc = O.dispatch_row(wl.x.values[row_src[r]], cfg.payload)
+        assert np.array_equal(g_rows[i], pay), f"row {r}"
+        if g_sc is not None:
+            assert np.array_equal(g_sc[i], sc), f"scales of row {r}"
+    note(f"route {name}: max|dlogit|={dl:.2e} near-ties={near} "
+         f"plan={'oracle' if same else 'own top-k'}")
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -155,6 +177,44 @@ INT_CASES = {
     # many tokens (LDS-staged partial gate)
     "int_t4096_e256": C["dsv3_decode"].with_shape(T=4096, H=256, E=256, k=8),
 }
+# The route's own plan on the paths that build the tile histogram inside the
+# gate's top-k epilogue, compared through dispatch, fixture and combine on
+# sampled rows and tokens: the DeepSeek-V3 prefill shape itself (LDS-staged
+# split gate, 64-token reduction workgroups with the fused histogram, fp8
+# payload, dual residual), the first size with fused-histogram reduction
+# workgroups at 384 experts, more than 16384 tokens, and the one-pass gate
+# (hidden dimension not split: H = 64 at few and many tokens, and more
+# tokens than the partial-logit workspace holds).
+INT_LARGE = {
+    "int_dsv3_prefill": C["dsv3_prefill"],
+    "int_fused_t16321_e384": C["moonep_skew"].with_shape(T=16321, H=256,
+                                                        zipf_bias=False),
+    "int_t20000": C["dsv3_prefill"].with_shape(T=20000, H=512),
+    "int_onepass_t300_e512_k16": C["moonep_skew"].with_shape(
+        T=300, H=64, E=512, k=16, pad=8, zipf_bias=False),
+    "int_onepass_t5000_h64": C["dsv3_decode"].with_shape(T=5000, H=64),
+    "int_onepass_t70000": C["mixtral"].with_shape(T=70000, H=128, E=64, k=4,
+                                                  pad=16),
+}
+
+
+def _integer_chain(cfg, name, full_check):
+    note(f"integer chain {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} "
+         f"payload={cfg.payload}")
+    wl = I.integer_workload(cfg, 3)
+    p, x = _route_gpu(wl)
+    torch.cuda.synchronize()
+    o = O.route(wl.x.values, wl.w_gate.values, None, cfg.k, cfg.pad)
+    gl = to_host(p["logits"])
+    assert np.array_equal(gl.astype(np.float64), o["logits"])
+    gi = to_host(p["topk_idx"])
+    check_topk_own_logits(gi, to_host(p["topk_w"]), gl, cfg.k)
+    assert np.array_equal(gi, o["topk_idx"])
+    np.testing.assert_allclose(to_host(p["topk_w"]), o["topk_w"], rtol=0,
+                               atol=2e-6)
+    assert np.array_equal(to_host(p["counts"]), o["counts"])
+    assert np.array_equal(to_host(p["offsets"]), o["offsets"])
+    _dispatch_combine_compare(wl, o, p, x, full_check=full_check)
 
 
 @pytest.mark.parametrize("name", list(INT_CASES))
@@ -162,18 +222,16 @@ def test_integer_inputs_bit_exact_chain(name):
     """Integer x and W in {-2..2}: logits are exact integers on both sides,
     ties are frequent, and the chain from the GPU's own routing must equal
     the oracle's exactly (combine within tolerance)."""
-    cfg = INT_CASES[name]
-    note(f"integer chain {name}")
-    wl = I.integer_workload(cfg, 3)
-    p, x = _route_gpu(wl)
-    o = O.route(wl.x.values, wl.w_gate.values, None, cfg.k, cfg.pad)
-    assert np.array_equal(to_host(p["logits"]).astype(np.float64), o["logits"])
-    assert np.array_equal(to_host(p["topk_idx"]), o["topk_idx"])
-    np.testing.assert_allclose(to_host(p["topk_w"]), o["topk_w"], rtol=0,
-                               atol=2e-6)
-    assert np.array_equal(to_host(p["counts"]), o["counts"])
-    assert np.array_equal(to_host(p["offsets"]), o["offsets"])
-    _dispatch_combine_compare(wl, o, p, x, full_check=True)
+    _integer_chain(INT_CASES[name], name, full_check=True)
+
+
+@pytest.mark.parametrize("name", list(INT_LARGE))
+def test_integer_route_plan_chain_large(name):
+    """As above at sizes up to the full DeepSeek-V3 prefill shape: the slot
+    plan moe_route writes (tile bases and ranks from its own epilogue)
+    drives moe_dispatch, and tok_row / row_src must equal the oracle's in
+    full; rows, scales, expert outputs and the combine on samples."""
+    _integer_chain(INT_LARGE[name], name, full_check=False)
 
 
 # ------------------------------------------------------------------ dispatch
