@@ -94,55 +94,189 @@ def algorithmic_bytes(cfg):
     return dict(route=route, dispatch=dispatch, combine=combine)
 
 
-def cpu_baseline(cfg, wl, n_tokens):
-    """The oracle, single-threaded, on the first n_tokens tokens of the same
-    workload (same H, E, k, pad, payload, expert and residual)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _shared_array(shape, dtype):
+    """Zeroed array in anonymous shared memory: workers forked after its
+    creation write into the same pages the parent reads."""
+    import mmap
+    n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+    buf = mmap.mmap(-1, max(n, 1))
+    return np.frombuffer(buf, dtype=dtype, count=int(np.prod(shape))).reshape(
+        shape)
+
+
+# Inputs and outputs of the CPU-baseline stages, set before the worker pool
+# is forked so that the workers inherit them.
+_CPU = {}
+
+
+def _cpu_route(span):
+    from oracle import moe_oracle as O
+    c = _CPU
+    lo, hi = span
+    logits = O.gate_logits(c["x"][lo:hi], c["w"], c["bias"])
+    idx, w = O.select_topk(logits, c["k"])
+    c["idx"][lo:hi] = idx
+    c["tw"][lo:hi] = w
+
+
+def _cpu_dispatch(span):
+    from oracle import moe_oracle as O
+    c = _CPU
+    lo, hi = span
+    rows, scales = O.dispatch_rows(c["x"], c["row_src"][lo:hi], c["payload"])
+    c["rows"][lo:hi] = rows
+    if scales is not None:
+        c["scales"][lo:hi] = scales
+
+
+def _cpu_fixture(span):
+    from oracle import moe_oracle as O
+    c = _CPU
+    lo, hi = span
+    for r in range(lo, hi):
+        if c["row_src"][r] < 0:
+            continue
+        e = O.expert_of_row(c["offsets"], r)
+        yv = O.expert_fixture_row(c["rows"][r], None if c["scales"] is None
+                                  else c["scales"][r], c["sigma"][e],
+                                  c["payload"], c["y_dtype"])
+        c["y"][r] = yv if c["y_dtype"] == "f32" else O.bf16_value(yv)
+
+
+def _cpu_combine(span):
+    from oracle import moe_oracle as O
+    c = _CPU
+    lo, hi = span
+    k, H = c["k"], c["y"].shape[1]
+    g = max(1, 65536 // (k * H))      # tokens per call: cache-sized arrays
+    for a in range(lo, hi, g):
+        b = min(hi, a + g)
+        tr = c["tok_row"][a:b]
+        n = b - a
+        routed = O.combine(c["y"][tr.ravel()], np.arange(n * k).reshape(n, k),
+                           c["tw"][a:b])
+        if c["residual"] is not None:
+            res, rnr, _ = O.farskip_update(routed, c["shared"][a:b],
+                                           c["residual"][a:b])
+            c["out"][a:b] = res
+            c["rnr"][a:b] = rnr
+        else:
+            c["out"][a:b] = O.routed_output(routed, c["y_dtype"]).view(
+                c["out"].dtype)
+
+
+def _spans(n, parts):
+    step = max(1, -(-n // parts))
+    return [(a, min(n, a + step)) for a in range(0, n, step)]
+
+
+def cpu_baseline(cfg, wl, n_tokens, workers):
+    """The oracle on the first n_tokens tokens of the same workload (same H,
+    E, k, pad, payload, expert and residual), timed twice on the host cores:
+    one thread, then split over ``workers`` forked processes (tokens for the
+    route and combine, rows for the dispatch; each worker single-threaded).
+    Both runs call the same oracle functions on chunks of tokens or rows;
+    every token and row is computed on its own, so the results are the
+    same.  Must run before the GPU is initialised (the workers are
+    forked)."""
+    import multiprocessing as mp
     from threadpoolctl import threadpool_limits
-    from combine_router_gate_amd import inputs as I
     from oracle import moe_oracle as O
 
     sub = cfg.with_shape(T=n_tokens)
-    x = wl.x.values[:n_tokens]
-    with threadpool_limits(limits=1):
+    T, H, E, k, pad = sub.T, sub.H, sub.E, sub.k, sub.pad
+    cap = O.rows_capacity(T, E, k, pad)
+    pdt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[sub.payload]
+    c = _CPU
+    c.clear()
+    c.update(x=wl.x.values[:T], w=wl.w_gate.values, bias=wl.bias, k=k,
+             payload=sub.payload, y_dtype=sub.y_dtype, sigma=wl.sigma,
+             shared=(wl.shared.values[:T] if wl.shared is not None else None),
+             residual=(wl.residual.values[:T] if wl.residual is not None
+                       else None))
+    c["idx"] = _shared_array((T, k), np.int32)
+    c["tw"] = _shared_array((T, k), np.float32)
+    c["rows"] = _shared_array((cap, H), pdt)
+    c["scales"] = (_shared_array((cap, H // 128), np.float32)
+                   if sub.payload == "fp8" else None)
+    c["y"] = _shared_array((cap, H), np.float32)
+    c["out"] = _shared_array((T, H), np.float32 if (
+        sub.y_dtype == "f32" and not sub.residual) else np.uint16)
+    c["rnr"] = _shared_array((T, H), np.uint16)
+    c["tok_row"] = _shared_array((T, k), np.int32)
+    c["row_src"] = _shared_array((cap,), np.int32)
+    c["offsets"] = _shared_array((E + 1,), np.int32)
+
+    def run(pool, n_chunks):
+        go = (lambda f, spans: pool.map(f, spans)) if pool is not None else \
+            (lambda f, spans: [f(sp) for sp in spans])
         t0 = time.perf_counter()
-        r = O.route(x, wl.w_gate.values, wl.bias, sub.k, sub.pad)
+        go(_cpu_route, _spans(T, n_chunks))
+        counts = O.expert_counts(c["idx"], E)
+        offsets = O.padded_offsets(counts, pad)
         t1 = time.perf_counter()
-        cap = O.rows_capacity(sub.T, sub.E, sub.k, sub.pad)
-        tok_row, row_src = O.assign_slots(r["topk_idx"], r["offsets"], sub.E,
-                                          cap)
-        rows, scales = O.dispatch_rows(x, row_src, sub.payload)
+        tok_row, row_src = O.assign_slots(c["idx"], offsets, E, cap)
+        c["tok_row"][:] = tok_row
+        c["row_src"][:] = row_src
+        c["offsets"][:] = offsets
+        go(_cpu_dispatch, _spans(cap, n_chunks))
         t2 = time.perf_counter()
-        # stand-in expert (not timed, as on the GPU)
-        yrows = {}
-        for t in range(sub.T):
-            for j in range(sub.k):
-                rr = int(tok_row[t, j])
-                e = O.expert_of_row(r["offsets"], rr)
-                yv = O.expert_fixture_row(rows[rr], None if scales is None
-                                          else scales[rr], wl.sigma[e],
-                                          sub.payload, sub.y_dtype)
-                yrows[rr] = yv if sub.y_dtype == "f32" else O.bf16_value(yv)
+        go(_cpu_fixture, _spans(cap, n_chunks))         # stand-in expert
         t3 = time.perf_counter()
-        routed = np.stack([O.combine_token(
-            np.stack([yrows[int(rr)] for rr in tok_row[t]]), r["topk_w"][t])
-            for t in range(sub.T)])
-        if sub.residual:
-            O.farskip_update(routed, wl.shared.values[:n_tokens],
-                             wl.residual.values[:n_tokens])
-        else:
-            O.routed_output(routed, sub.y_dtype)
+        go(_cpu_combine, _spans(T, n_chunks))
         t4 = time.perf_counter()
+        return t1 - t0, t2 - t1, t4 - t3
+
     b = algorithmic_bytes(sub)
-    dc_s = (t2 - t1) + (t4 - t3)
+    with threadpool_limits(limits=1):
+        print(f"cpu baseline: one thread, {T} tokens", file=sys.stderr,
+              flush=True)
+        one = run(None, 16)
+        first = {key: c[key].copy() for key in ("idx", "out", "rnr")}
+        print(f"cpu baseline: {workers} processes", file=sys.stderr,
+              flush=True)
+        ctx = mp.get_context("fork")
+        with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+            allc = run(pool, 4 * workers)
+    for key, v in first.items():      # the two runs computed the same
+        assert np.array_equal(c[key], v), key
+    c.clear()
+
+    def rate(t):
+        return round((b["dispatch"] + b["combine"]) / (t[1] + t[2]) / 1e9, 4)
     return {
-        "value": round((b["dispatch"] + b["combine"]) / dc_s / 1e9, 4),
-        "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "value": rate(allc), "unit": "GB/s", "cores": workers,
+        "kind": "oracle",
         "sample": (f"first {n_tokens} of {cfg.T} tokens of the {cfg.name} "
                    f"workload (H={cfg.H}, E={cfg.E}, k={cfg.k}, pad={cfg.pad}, "
-                   f"payload={cfg.payload}); numpy fp64 oracle, one thread"),
-        "route_s": round(t1 - t0, 3), "dispatch_s": round(t2 - t1, 3),
-        "combine_s": round(t4 - t3, 3),
+                   f"payload={cfg.payload}); numpy fp64 oracle split over "
+                   f"{workers} single-threaded processes (dispatch + combine "
+                   f"bytes over their time; route and the stand-in expert "
+                   f"timed apart)"),
+        "cpu_model": _cpu_model(),
+        "route_s": round(allc[0], 3), "dispatch_s": round(allc[1], 3),
+        "combine_s": round(allc[2], 3),
+        "single_thread": {"value": rate(one), "unit": "GB/s", "cores": 1,
+                          "route_s": round(one[0], 3),
+                          "dispatch_s": round(one[1], 3),
+                          "combine_s": round(one[2], 3)},
     }
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
 
 
 def _mean_ms(pairs):
@@ -168,6 +302,31 @@ def measure_cold(step, stream, dev, iters=10, flush_mb=1024):
         "combine_us": round(_mean_ms([(e[2], e[3]) for e in evs]) * 1e3, 2),
         "iters": iters, "flush_mib": flush_mb,
     }
+
+
+def measure_copy(stream, dev, mib=1024, iters=10):
+    """A plain device-to-device copy of mib MiB (torch copy_, on the launch
+    stream) timed in the same session: the bandwidth an HBM-bound kernel on
+    this box can be held against besides the nominal peak."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(iters):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / iters
+    del src, dst
+    return {"gbs": round(2 * n / (us * 1e-6) / 1e9, 1), "us": round(us, 2),
+            "bytes_moved": 2 * n,
+            "how": f"torch copy_ of {mib} MiB device to device, mean of "
+                   f"{iters}"}
 
 
 def measure_backward(cfg, moe, y, tok_row, topk_w, stream, dev, iters=10):
@@ -386,9 +545,12 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the backward and FarSkip-overlap measurements "
                     "that follow the timed steps")
-    ap.add_argument("--cold-cache", action="store_true",
-                    help="also time the stages with L2 and MALL flushed "
+    ap.add_argument("--no-cold-cache", action="store_true",
+                    help="skip the stage times with L2 and MALL flushed "
                     "before every iteration")
+    ap.add_argument("--workers", type=int,
+                    default=min(16, len(os.sched_getaffinity(0))),
+                    help="host processes of the all-cores CPU-oracle run")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one plain device-to-device copy of this many "
                     "MiB before timing (reference for byte counters)")
@@ -398,12 +560,18 @@ def main():
               "no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import torch
     from combine_router_gate_amd import inputs as I
-    from combine_router_gate_amd import moe
 
     cfg = I.CONFIGS[args.config]
     wl = I.make_workload(cfg, args.seed)
+    # the CPU-oracle baseline first: its worker processes are forked, which
+    # must happen before this process initialises the GPU
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(cfg, wl, min(args.cpu_tokens, cfg.T), args.workers)
+
+    import torch
+    from combine_router_gate_amd import moe
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -538,8 +706,16 @@ def main():
     dc = (d_ms + c_ms) * 1e3
     line["dc_us_p10_p50_p90"] = [round(float(np.percentile(dc, q)), 2)
                                  for q in (10, 50, 90)]
-    if args.cold_cache:
-        line["cold_cache"] = measure_cold(step, stream, dev)
+    copy = measure_copy(stream, dev)
+    line["copy_bw"] = copy
+    line["dc_frac_of_copy"] = round(dc_gbs / copy["gbs"], 4)
+    if not args.no_cold_cache:
+        cold = measure_cold(step, stream, dev)
+        cdc = cold["dispatch_us"] + cold["combine_us"]
+        cgbs = (b["dispatch"] + b["combine"]) / (cdc * 1e-6) / 1e9
+        cold.update(dc_us=round(cdc, 2), dc_gbs=round(cgbs, 1),
+                    dc_pct_of_peak=round(100.0 * cgbs / PEAK_HBM_GBS, 1))
+        line["cold_cache"] = cold
     if not args.no_extras:
         def layer():   # the timed step's launches, on the current stream
             moe.moe_route(x, w, bias, k, pad, p["topk_idx"], p["topk_w"],
@@ -560,9 +736,8 @@ def main():
             line["farskip_overlap"] = measure_farskip_overlap(
                 cfg, moe, y, d["tok_row"], p["topk_w"], shared, resid,
                 stream, dev)
-    if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, wl, min(args.cpu_tokens,
-                                                         cfg.T))
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -212,7 +212,8 @@ def e4m3_encode(v) -> np.ndarray:
 def quantize_row_e4m3(x_row):
     """Quantise one hidden row to fp8 with one float32 scale per block of 128
     consecutive elements: a = max |x| over the block, s = fl32(a / 448)
-    (s = 1 when a = 0), code = E4M3(fl32(x / s)).  Returns (codes, scales)."""
+    (s = 1 when a = 0), code = E4M3(fl32(x / s)).  Returns (codes, scales).
+    A [n, H] array is n rows, each quantised on its own."""
     x = np.asarray(x_row, dtype=np.float32)
     H = x.shape[-1]
     assert H % FP8_BLOCK == 0
@@ -221,14 +222,16 @@ def quantize_row_e4m3(x_row):
     scales = np.where(amax > 0, amax / np.float32(FP8_MAX),
                       np.float32(1.0)).astype(np.float32)
     q = (blocks / scales[:, None]).astype(np.float32)   # float32 quotient
-    return e4m3_encode(q).reshape(H), scales
+    return (e4m3_encode(q).reshape(x.shape),
+            scales.reshape(x.shape[:-1] + (H // FP8_BLOCK,)))
 
 
 # ---------------------------------------------------------------- O6 rows
 
 def dispatch_row(x_row, payload: str):
     """Payload written for one token row: an exact copy for "f32" (float32
-    values) and "bf16" (bf16 bits), or (codes, scales) for "fp8"."""
+    values) and "bf16" (bf16 bits), or (codes, scales) for "fp8".  A [n, H]
+    array gives the payloads of n rows."""
     if payload == "f32":
         return np.asarray(x_row, dtype=np.float32).copy(), None
     if payload == "bf16":
@@ -238,21 +241,27 @@ def dispatch_row(x_row, payload: str):
     raise ValueError(payload)
 
 
-def dispatch_rows(x, row_src, payload: str):
+def dispatch_rows(x, row_src, payload: str, chunk: int = 0):
     """O6 for every valid row of the expert-major buffer: row r receives the
-    payload of token row_src[r].  Rows with row_src = -1 are left zero (their
-    content is unspecified by definition and never compared)."""
+    payload of token row_src[r] (each row exactly as ``dispatch_row`` gives
+    it; rows are taken ``chunk`` at a time, by default as many as keep the
+    temporaries near 32K elements).  Rows with row_src = -1 are left zero
+    (their content is unspecified by definition and never compared)."""
     x = np.asarray(x, dtype=np.float32)
-    R, H = len(row_src), x.shape[1]
+    src = np.asarray(row_src)
+    R, H = len(src), x.shape[1]
+    chunk = chunk if chunk > 0 else max(1, 32768 // H)
     dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[payload]
     rows = np.zeros((R, H), dtype=dt)
     scales = (np.zeros((R, H // FP8_BLOCK), dtype=np.float32)
               if payload == "fp8" else None)
-    for r in np.nonzero(np.asarray(row_src) >= 0)[0]:
-        p, s = dispatch_row(x[row_src[r]], payload)
-        rows[r] = p
+    valid = np.nonzero(src >= 0)[0]
+    for i in range(0, len(valid), chunk):
+        rr = valid[i:i + chunk]
+        p, s = dispatch_row(x[src[rr]], payload)
+        rows[rr] = p
         if scales is not None:
-            scales[r] = s
+            scales[rr] = s
     return rows, scales
 
 

@@ -333,6 +333,32 @@ def test_farskip_golden():
         assert O.bf16_value(rnr)[0] == want_rnr
 
 
+def test_dispatch_rows_equal_each_row_alone():
+    """dispatch_rows handles rows in chunks of arrays; every row must still
+    equal the single-row definition (quantize_row_e4m3 / bit copy), across
+    chunk boundaries and with padding rows in between."""
+    rng = np.random.default_rng(5)
+    x = I.bf16_bits_to_f32(I.f32_to_bf16_bits(
+        rng.standard_normal((40, 256)).astype(np.float32)))
+    x[3, 128:] = 0.0
+    row_src = np.full(97, -1, dtype=np.int32)
+    pos = rng.choice(97, 60, replace=False)
+    row_src[pos] = rng.integers(0, 40, size=60)
+    for payload in ("fp8", "bf16", "f32"):
+        rows, scales = O.dispatch_rows(x, row_src, payload, chunk=7)
+        for r in range(97):
+            if row_src[r] < 0:
+                assert not rows[r].any()
+                continue
+            p, sc = O.dispatch_row(x[row_src[r]], payload)
+            assert np.array_equal(rows[r], p)
+            if payload == "fp8":
+                assert np.array_equal(scales[r], sc)
+                c1, s1 = O.quantize_row_e4m3(x[row_src[r]])
+                assert np.array_equal(rows[r], c1) and np.array_equal(
+                    scales[r], s1)
+
+
 def _chain(cfg, seed=0, sigma_set=None):
     wl = I.make_workload(cfg, seed, sigma_set=sigma_set)
     x = wl.x.values
