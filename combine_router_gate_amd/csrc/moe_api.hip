@@ -86,6 +86,9 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes";
     case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output overlaps an input or another output";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "MOE_ERR_SCRATCH: T, E, k need more than the static scratch of "
+             "moe_dispatch_noalloc (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown moe_status";
   }
 }
@@ -159,13 +162,19 @@ int moe_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
                                      workspace, (hipStream_t)stream));
 }
 
-int moe_dispatch(const void* x, int x_dtype, int T, int H,
-                 const int32_t* topk_idx, int k, int E, int pad,
-                 const int32_t* counts, const int32_t* offsets,
-                 const void* workspace, size_t workspace_bytes,
-                 int payload_dtype, void* rows, size_t rows_capacity,
-                 float* row_scales, int32_t* row_src, int32_t* tok_row,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by moe_dispatch (need_ws: a workspace of
+// workspace_bytes is one more input) and moe_dispatch_noalloc (none).
+int check_dispatch(const void* x, int x_dtype, int T, int H,
+                   const int32_t* topk_idx, int k, int E, int pad,
+                   const int32_t* counts, const int32_t* offsets,
+                   bool need_ws, const void* workspace,
+                   size_t workspace_bytes, int payload_dtype, void* rows,
+                   size_t rows_capacity, float* row_scales, int32_t* row_src,
+                   int32_t* tok_row) {
   int st = check_route_shape(T, E, k, pad);
   if (st != MOE_OK) return st;
   if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
@@ -176,8 +185,9 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
   if (counts == nullptr || offsets == nullptr || row_src == nullptr)
     return MOE_ERR_NULL;
   if (fp8 != (row_scales != nullptr)) return fp8 ? MOE_ERR_NULL : MOE_ERR_DTYPE;
-  if (T > 0 && (x == nullptr || topk_idx == nullptr || workspace == nullptr ||
-                rows == nullptr || tok_row == nullptr))
+  if (T > 0 && (x == nullptr || topk_idx == nullptr ||
+                (need_ws && workspace == nullptr) || rows == nullptr ||
+                tok_row == nullptr))
     return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(rows, 16) || !aligned(topk_idx, 4) ||
       !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(workspace, 16) ||
@@ -185,16 +195,37 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
     return MOE_ERR_ALIGN;
   if (rows_capacity < moe_rows_capacity(T, E, k, pad)) return MOE_ERR_CAPACITY;
   if (rows_capacity > 0x7fffffffULL) return MOE_ERR_SHAPE;
-  if (workspace_bytes < moe::workspace_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+  if (need_ws && workspace_bytes < moe::workspace_bytes(T, E, k))
+    return MOE_ERR_WORKSPACE;
   const size_t xs = dtype_size(x_dtype), ps = dtype_size(payload_dtype);
   const Span ins[] = {{x, (size_t)T * H * xs}, {topk_idx, (size_t)T * k * 4},
                       {counts, (size_t)E * 4}, {offsets, (size_t)(E + 1) * 4},
-                      {workspace, moe::workspace_bytes(T, E, k)}};
+                      {workspace,
+                       need_ws ? moe::workspace_bytes(T, E, k) : 0}};
   const Span outs[] = {{rows, rows_capacity * H * ps},
                        {row_scales, fp8 ? rows_capacity * (H / 128) * 4 : 0},
                        {row_src, rows_capacity * 4},
                        {tok_row, (size_t)T * k * 4}};
   if (any_overlap(outs, 4, ins, 5)) return MOE_ERR_ALIAS;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch(const void* x, int x_dtype, int T, int H,
+                 const int32_t* topk_idx, int k, int E, int pad,
+                 const int32_t* counts, const int32_t* offsets,
+                 const void* workspace, size_t workspace_bytes,
+                 int payload_dtype, void* rows, size_t rows_capacity,
+                 float* row_scales, int32_t* row_src, int32_t* tok_row,
+                 void* stream) {
+  const int st = check_dispatch(x, x_dtype, T, H, topk_idx, k, E, pad,
+                                counts, offsets, true, workspace,
+                                workspace_bytes, payload_dtype, rows,
+                                rows_capacity, row_scales, row_src, tok_row);
+  if (st != MOE_OK) return st;
   if (trace_on())
     std::fprintf(stderr, "moe_dispatch T=%d H=%d E=%d k=%d payload=%d cap=%zu\n",
                  T, H, E, k, payload_dtype, rows_capacity);
@@ -203,6 +234,36 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
       x, x_dtype, T, H, topk_idx, k, E, counts, offsets, workspace,
       payload_dtype, rows, rows_capacity, row_scales, row_src, tok_row,
       (hipStream_t)stream));
+}
+
+size_t moe_noalloc_scratch_bytes(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK)
+    return 0;
+  return moe::noalloc_bytes(T, E, k);
+}
+
+int moe_dispatch_noalloc(const void* x, int x_dtype, int T, int H,
+                         const int32_t* topk_idx, int k, int E, int pad,
+                         const int32_t* counts, const int32_t* offsets,
+                         int payload_dtype, void* rows, size_t rows_capacity,
+                         float* row_scales, int32_t* row_src,
+                         int32_t* tok_row, void* stream) {
+  const int st = check_dispatch(x, x_dtype, T, H, topk_idx, k, E, pad,
+                                counts, offsets, false, nullptr, 0,
+                                payload_dtype, rows, rows_capacity,
+                                row_scales, row_src, tok_row);
+  if (st != MOE_OK) return st;
+  if (moe::noalloc_bytes(T, E, k) > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_SCRATCH;
+  if (trace_on())
+    std::fprintf(stderr,
+                 "moe_dispatch_noalloc T=%d H=%d E=%d k=%d payload=%d "
+                 "cap=%zu\n",
+                 T, H, E, k, payload_dtype, rows_capacity);
+  if (T == 0 && rows_capacity == 0) return MOE_OK;
+  return hip_status(moe::launch_dispatch_noalloc(
+      x, x_dtype, T, H, topk_idx, k, E, pad, counts, offsets, payload_dtype,
+      rows, rows_capacity, row_scales, row_src, tok_row, (hipStream_t)stream));
 }
 
 int moe_combine_residual(const void* y, int y_dtype, int H, size_t y_rows,

@@ -55,6 +55,13 @@ inline size_t workspace_bytes(int T, int E, int k) {
                       ws_partial_bytes(T, E);
 }
 
+// Bytes of the static scratch moe_dispatch_noalloc uses: the workspace's
+// tile bases and ranks, then a plan's own counts and offsets.
+inline size_t noalloc_bytes(int T, int E, int k) {
+  return ws_tile_bytes(T, E) + ws_rank_bytes(T, k) + align256(size_t(E) * 4) +
+         align256(size_t(E + 1) * 4);
+}
+
 // dtype codes of moe.h
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
@@ -75,6 +82,15 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
                            const void* workspace, int pdt, void* rows,
                            size_t capacity, float* row_scales,
                            int32_t* row_src, int32_t* tok_row, hipStream_t s);
+
+// moe_dispatch with its tile plan rebuilt in the library's static scratch
+hipError_t launch_dispatch_noalloc(const void* x, int xdt, int T, int H,
+                                   const int32_t* topk_idx, int k, int E,
+                                   int pad, const int32_t* counts,
+                                   const int32_t* offsets, int pdt, void* rows,
+                                   size_t capacity, float* row_scales,
+                                   int32_t* row_src, int32_t* tok_row,
+                                   hipStream_t s);
 
 hipError_t launch_combine(const void* y, int ydt, int H, size_t y_rows,
                           const int32_t* tok_row, const float* topk_w, int T,

@@ -6,7 +6,7 @@ current HIP stream.  There is no fallback: if the library is not built this
 module raises on first use.
 
 Low-level functions carry the C names (``moe_route``, ``moe_plan``,
-``moe_dispatch``, ``moe_combine_residual``, ``moe_farskip_aux``,
+``moe_dispatch``, ``moe_dispatch_noalloc``, ``moe_combine_residual``, ``moe_farskip_aux``,
 ``moe_combine_backward``, ``moe_dispatch_backward``, ``moe_expert_gemm_fp8``,
 ``moe_expert_fixture``) and take preallocated tensors; ``route`` / ``plan`` /
 ``dispatch`` / ``combine_residual`` / ``farskip_aux`` /
@@ -43,6 +43,9 @@ _SIGS = {
     "moe_plan": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "moe_dispatch": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp,
                           _sz, _i, _vp, _sz, _vp, _vp, _vp, _vp]),
+    "moe_noalloc_scratch_bytes": (_sz, [_i, _i, _i]),
+    "moe_dispatch_noalloc": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp,
+                                  _i, _vp, _sz, _vp, _vp, _vp, _vp]),
     "moe_combine_residual": (_i, [_vp, _i, _i, _sz, _vp, _vp, _i, _i, _vp,
                                   _vp, _vp, _vp, _vp, _i, _vp]),
     "moe_expert_fixture": (_i, [_vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz,
@@ -168,6 +171,22 @@ def moe_dispatch(x, topk_idx, E, pad, counts, offsets, workspace,
                             stream if stream is not None else
                             _stream(x.device))
     _check(st, "moe_dispatch")
+
+
+def moe_noalloc_scratch_bytes(T: int, E: int, k: int) -> int:
+    return lib().moe_noalloc_scratch_bytes(T, E, k)
+
+
+def moe_dispatch_noalloc(x, topk_idx, E, pad, counts, offsets, payload_dtype,
+                         rows, row_scales, row_src, tok_row, stream=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    st = lib().moe_dispatch_noalloc(
+        _ptr(x), _dt(x), T, H, _ptr(topk_idx), k, E, pad, _ptr(counts),
+        _ptr(offsets), payload_dtype, _ptr(rows), rows.shape[0],
+        _ptr(row_scales), _ptr(row_src), _ptr(tok_row),
+        stream if stream is not None else _stream(x.device))
+    _check(st, "moe_dispatch_noalloc")
 
 
 def moe_combine_residual(y, tok_row, topk_w, shared, residual_in,

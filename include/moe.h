@@ -11,6 +11,9 @@
  *   moe_dispatch         stable scatter of token rows into an expert-major
  *                        buffer padded per expert (optionally OCP fp8 E4M3
  *                        with one fp32 scale per 1x128 block)
+ *   moe_dispatch_noalloc the same with no workspace argument (its scratch is
+ *                        a static device array), for callers that cannot
+ *                        allocate
  *   moe_combine_residual weighted gather-combine back to token order, fused
  *                        with the FarSkip-Collective dual residual update
  *   moe_farskip_aux      the auxiliary residual stream alone (split form)
@@ -25,7 +28,8 @@
  * Conventions shared by every entry point
  *   - Device pointers.  Every array argument is device memory (HBM) that the
  *     caller allocated and owns; the library never allocates, frees or keeps
- *     a pointer after the call returns.  Arrays are dense row-major with the
+ *     a pointer after the call returns.  Its only device memory of its own
+ *     is the static scratch array of moe_dispatch_noalloc.  Arrays are dense row-major with the
  *     shapes given below.  Arrays read or written as 16-byte vectors (x,
  *     w_gate, rows, y, shared, residuals, out, gradients of those, workspace)
  *     need 16-byte aligned base addresses; the others their element size.
@@ -44,7 +48,8 @@
  *   - Determinism.  No floating-point atomics are used: identical inputs give
  *     bit-identical outputs on every run.
  *   - Thread safety.  The library keeps no mutable state besides the last
- *     HIP error code (thread-local).
+ *     HIP error code (thread-local) and, for moe_dispatch_noalloc, its
+ *     static scratch array and that array's device address per GPU.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -73,7 +78,9 @@ typedef enum {
   MOE_ERR_CAPACITY = -5,  /* rows_capacity < moe_rows_capacity(T, E, k, pad) */
   MOE_ERR_WORKSPACE = -6, /* workspace_bytes < moe_workspace_bytes(T, E, k)  */
   MOE_ERR_ALIAS = -7,     /* an output overlaps an input it may not alias   */
-  MOE_ERR_HIP = -8        /* a kernel launch failed                         */
+  MOE_ERR_HIP = -8,       /* a kernel launch failed                         */
+  MOE_ERR_SCRATCH = -9    /* sizes need more than the library's static
+                             scratch (MOE_NOALLOC_SCRATCH_BYTES)            */
 } moe_status;
 
 /* Static description of a status code (never NULL). */
@@ -198,6 +205,35 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
                  void* rows, size_t rows_capacity, float* row_scales,
                  int32_t* row_src, int32_t* tok_row,
                  void* stream);
+
+/*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc) and have no workspace to hand over: same arguments and outputs
+ * as moe_dispatch without workspace / workspace_bytes, bit-identical rows,
+ * row_scales, row_src and tok_row.  The tile plan moe_dispatch reads from the
+ * workspace (per-(tile, expert) first rows, per-slot ranks) is rebuilt from
+ * topk_idx in a static device array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; nothing is
+ * allocated or freed.  That array is shared by every call on the same GPU:
+ * calls that overlap on one GPU (other streams, other host threads) race on
+ * it and must be serialised by the caller.  Its contents do not carry over
+ * between calls (each call rewrites what it reads).
+ * Limit: moe_noalloc_scratch_bytes(T, E, k) <= MOE_NOALLOC_SCRATCH_BYTES
+ * (8 MiB: about 4 bytes per slot plus 4 bytes per expert per 64 tokens;
+ * 65536 tokens fit for every E <= 512 and k <= 16), else MOE_ERR_SCRATCH
+ * before anything is enqueued.  Other errors as for moe_dispatch; MOE_ERR_HIP also
+ * if the array's device address cannot be obtained.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+size_t moe_noalloc_scratch_bytes(int T, int E, int k);
+int moe_dispatch_noalloc(const void* x, int x_dtype, int T, int H,
+                         const int32_t* topk_idx, int k, int E, int pad,
+                         const int32_t* counts, const int32_t* offsets,
+                         int payload_dtype,
+                         void* rows, size_t rows_capacity, float* row_scales,
+                         int32_t* row_src, int32_t* tok_row,
+                         void* stream);
 
 /*
  * moe_combine_residual -- weighted gather-combine fused with the FarSkip

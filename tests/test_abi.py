@@ -16,6 +16,7 @@ from combine_router_gate_amd import build as B
 from oracle import moe_oracle as O
 
 OK, NULL, SHAPE, DTYPE, ALIGN, CAP, WS, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+SCRATCH = -9
 
 
 @pytest.fixture(scope="module")
@@ -44,7 +45,7 @@ def test_exports_every_header_symbol(L):
 
 
 def test_status_strings(L):
-    for s in [OK, NULL, SHAPE, DTYPE, ALIGN, CAP, WS, ALIAS, -8]:
+    for s in [OK, NULL, SHAPE, DTYPE, ALIGN, CAP, WS, ALIAS, -8, SCRATCH]:
         txt = moe.moe_status_string(s)
         assert txt and "unknown" not in txt
     assert "unknown" in moe.moe_status_string(-99)
@@ -137,6 +138,52 @@ def _dispatch(L, **kw):
 ])
 def test_dispatch_validation(L, no_gpu, kw, want):
     assert _dispatch(L, **kw) == want
+
+
+def _dispatch_noalloc(L, **kw):
+    a = dict(x=A[0], xdt=1, T=100, H=256, idx=A[1], k=2, E=16, pad=4,
+             counts=A[2], offsets=A[3], pdt=1, rows=A[5],
+             cap=O.rows_capacity(100, 16, 2, 4), scales=None, row_src=A[6],
+             tok_row=A[7], stream=None)
+    a.update(kw)
+    return L.moe_dispatch_noalloc(
+        a["x"], a["xdt"], a["T"], a["H"], a["idx"], a["k"], a["E"], a["pad"],
+        a["counts"], a["offsets"], a["pdt"], a["rows"], a["cap"], a["scales"],
+        a["row_src"], a["tok_row"], a["stream"])
+
+
+def _noalloc_cap(T, E, k, pad):
+    return O.rows_capacity(T, E, k, pad)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(rows=None), NULL), (dict(row_src=None), NULL),
+    (dict(pdt=2), NULL), (dict(scales=A[8]), DTYPE), (dict(pdt=0), DTYPE),
+    (dict(pdt=2, scales=A[8], H=200), SHAPE),
+    (dict(cap=O.rows_capacity(100, 16, 2, 4) - 1), CAP),
+    (dict(rows=A[5] + 4), ALIGN), (dict(rows=A[0]), ALIAS),
+    (dict(tok_row=A[1]), ALIAS), (dict(k=0), SHAPE), (dict(E=513), SHAPE),
+    # more slots and tile counts than the 8 MiB static scratch holds
+    (dict(T=300000, H=8, k=8, E=16, cap=_noalloc_cap(300000, 16, 8, 4)),
+     SCRATCH),
+    (dict(T=90000, H=8, k=16, E=512, cap=_noalloc_cap(90000, 512, 16, 4)),
+     SCRATCH),
+])
+def test_dispatch_noalloc_validation(L, no_gpu, kw, want):
+    assert _dispatch_noalloc(L, **kw) == want
+
+
+def test_noalloc_scratch_limit(L):
+    limit = 8 << 20
+    # every E and k the library accepts fits at 65536 tokens
+    assert moe.moe_noalloc_scratch_bytes(65536, 512, 16) <= limit
+    assert moe.moe_noalloc_scratch_bytes(16384, 256, 8) <= limit
+    assert moe.moe_noalloc_scratch_bytes(300000, 16, 8) > limit
+    assert moe.moe_noalloc_scratch_bytes(4, 0, 1) == 0
+    # at least the tile bases and ranks the workspace would hold
+    for T, E, k in ((100, 16, 2), (16384, 256, 8), (65536, 512, 16)):
+        tiles = 4 * ((T + 63) // 64) * E + 4 * T * k
+        assert moe.moe_noalloc_scratch_bytes(T, E, k) >= tiles
 
 
 def _combine(L, **kw):
