@@ -9,7 +9,7 @@
 namespace moe {
 
 // Histogram tiles of the workspace for T tokens.
-inline int num_tiles(int T) { return (T + 63) / 64; }
+inline int num_tiles(int T) { return (int)(((long long)T + 63) / 64); }
 
 // Workspace layout (each array 256-byte aligned):
 //   tile_base [ntiles, E] int32  per-tile expert counts, then (after the
