@@ -430,6 +430,52 @@ def measure_expert_gemm(cfg, moe, d, p, dev, iters=5):
     }
 
 
+def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
+                           iters=20):
+    """Small batches: moe_route_dispatch (route + scatter, no plan kernel)
+    against moe_route followed by moe_dispatch, alone and as a whole layer
+    step with the combine; each timed over iters back-to-back launches."""
+    import torch
+    T, E, k, pad = cfg.T, cfg.E, cfg.k, cfg.pad
+    sp = stream.cuda_stream
+
+    def fused():
+        moe.moe_route_dispatch(x, w, bias, k, pad, p["topk_idx"],
+                               p["topk_w"], p["counts"], p["offsets"], None,
+                               p["workspace"], d["payload_dtype"], d["rows"],
+                               d["row_scales"], d["row_src"], d["tok_row"],
+                               sp)
+
+    def separate():
+        moe.moe_route(x, w, bias, k, pad, p["topk_idx"], p["topk_w"],
+                      p["counts"], p["offsets"], None, p["workspace"], sp)
+        moe.moe_dispatch(x, p["topk_idx"], E, pad, p["counts"], p["offsets"],
+                         p["workspace"], d["payload_dtype"], d["rows"],
+                         d["row_scales"], d["row_src"], d["tok_row"], sp)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    r = {"fused_us": timed(fused), "separate_us": timed(separate)}
+    r["fused_step_us"] = timed(lambda: (fused(), combine()))
+    r["separate_step_us"] = timed(lambda: (separate(), combine()))
+    r = {kk: round(v, 2) for kk, v in r.items()}
+    r["how"] = (f"{iters} back-to-back calls: route+dispatch in one call "
+                "(plan rebuilt in every scatter workgroup) vs moe_route then "
+                "moe_dispatch; step = with the combine")
+    return r
+
+
 def measure_graph(layer, stream, iters=20):
     """One layer (route + dispatch + combine) captured once into a HIP graph
     and replayed: µs per replay, against the same launches issued eagerly.
@@ -716,6 +762,12 @@ def main():
         cold.update(dc_us=round(cdc, 2), dc_gbs=round(cgbs, 1),
                     dc_pct_of_peak=round(100.0 * cgbs / PEAK_HBM_GBS, 1))
         line["cold_cache"] = cold
+    if not args.no_extras and T <= 512:
+        line["route_dispatch"] = measure_route_dispatch(
+            cfg, moe, x, w, bias, p, d, y,
+            lambda: moe.moe_combine_residual(y, d["tok_row"], p["topk_w"],
+                                             shared, resid, res_out, rnr,
+                                             out, sp), stream)
     if not args.no_extras:
         def layer():   # the timed step's launches, on the current stream
             moe.moe_route(x, w, bias, k, pad, p["topk_idx"], p["topk_w"],

@@ -53,53 +53,34 @@ __device__ __forceinline__ int token_row(
   return r;
 }
 
+// Rows past every expert's tokens: row_src = -1 for the padding rows of each
+// expert and every row from offsets[E] to capacity; fill block fb of nfb.
+__device__ __forceinline__ void fill_padding_rows(
+    int fb, int nfb, int E, const int32_t* counts, const int32_t* offsets,
+    long long capacity, int32_t* __restrict__ row_src) {
+  for (int e = fb; e < E; e += nfb) {
+    const long long hi = min((long long)offsets[e + 1], capacity);
+    for (long long r = (long long)offsets[e] + counts[e] + threadIdx.x;
+         r < hi; r += blockDim.x)
+      if (r >= 0) row_src[r] = -1;
+  }
+  for (long long r = max((long long)offsets[E], 0LL) + (long long)fb *
+                         blockDim.x + threadIdx.x;
+       r < capacity; r += (long long)nfb * blockDim.x)
+    row_src[r] = -1;
+}
+
 // MODE 0: exact copy (x and payload of the same 2- or 4-byte type)
 // MODE 1: bf16 x -> fp8;  MODE 2: fp32 x -> fp8
 // U: 64-lane chunks per lane step (2 keeps two loads in flight per lane; 1
 // lets few tokens spread over twice as many waves)
+// One wave's share (part of hsplit) of token t's row, copied or quantised to
+// every destination row rj[j] >= 0.
 template <int KMAX, int MODE, int U>
-__global__ __launch_bounds__(256) void dispatch_kernel(
-    const unsigned char* __restrict__ x, int esize, int T, int H,
-    const int32_t* __restrict__ topk_idx, int k, int E,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_base,
-    const int32_t* __restrict__ slot_rank, unsigned char* __restrict__ rows,
-    long long capacity, float* __restrict__ row_scales,
-    int32_t* __restrict__ row_src, int32_t* __restrict__ tok_row,
-    int tok_blocks, int hsplit) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if ((int)blockIdx.x >= tok_blocks) {
-    // padding rows of every expert, then every row past offsets[E]
-    const int fb = blockIdx.x - tok_blocks;
-    for (int e = fb; e < E; e += kDispatchFillBlocks) {
-      const long long hi = min((long long)offsets[e + 1], capacity);
-      for (long long r = (long long)offsets[e] + counts[e] + threadIdx.x;
-           r < hi; r += 256)
-        if (r >= 0) row_src[r] = -1;
-    }
-    for (long long r = max((long long)offsets[E], 0LL) + fb * 256 +
-                       threadIdx.x;
-         r < capacity; r += kDispatchFillBlocks * 256)
-      row_src[r] = -1;
-    return;
-  }
-  // wave -> (token, part): hsplit waves share one token's row (interleaved
-  // groups of 64-lane chunks); part 0 writes the metadata
-  const int gw = blockIdx.x * 4 + wv;
-  const int t = gw / hsplit, part = gw - t * hsplit;
-  if (t >= T) return;
-
-  const int r =
-      token_row(t, lane, k, E, capacity, topk_idx, tile_base, slot_rank);
-  if (lane < k && part == 0) {
-    tok_row[(size_t)t * k + lane] = r;
-    if (r >= 0) row_src[r] = t;
-  }
-  int rj[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    rj[j] = (j < k) ? __builtin_amdgcn_readlane(r, j) : -1;
-
+__device__ __forceinline__ void scatter_token_part(
+    const unsigned char* __restrict__ x, int esize, int H, int t, int part,
+    int hsplit, int lane, const int (&rj)[KMAX],
+    unsigned char* __restrict__ rows, float* __restrict__ row_scales) {
   if constexpr (MODE == 0) {
     const size_t rowb = (size_t)H * esize;
     const int nc = (int)(rowb / 16);
@@ -180,6 +161,168 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
       }
     }
   }
+}
+
+// Lane j < k holds row r of slot (t, j): record it (part 0 only) and
+// broadcast all k rows to every lane.
+template <int KMAX>
+__device__ __forceinline__ void publish_rows(int r, int t, int part, int lane,
+                                             int k, int32_t* __restrict__ row_src,
+                                             int32_t* __restrict__ tok_row,
+                                             int (&rj)[KMAX]) {
+  if (lane < k && part == 0) {
+    tok_row[(size_t)t * k + lane] = r;
+    if (r >= 0) row_src[r] = t;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    rj[j] = (j < k) ? __builtin_amdgcn_readlane(r, j) : -1;
+}
+
+template <int KMAX, int MODE, int U>
+__global__ __launch_bounds__(256) void dispatch_kernel(
+    const unsigned char* __restrict__ x, int esize, int T, int H,
+    const int32_t* __restrict__ topk_idx, int k, int E,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ slot_rank, unsigned char* __restrict__ rows,
+    long long capacity, float* __restrict__ row_scales,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ tok_row,
+    int tok_blocks, int hsplit) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if ((int)blockIdx.x >= tok_blocks) {
+    fill_padding_rows(blockIdx.x - tok_blocks, kDispatchFillBlocks, E, counts,
+                      offsets, capacity, row_src);
+    return;
+  }
+  // wave -> (token, part): hsplit waves share one token's row (interleaved
+  // groups of 64-lane chunks); part 0 writes the metadata
+  const int gw = blockIdx.x * 4 + wv;
+  const int t = gw / hsplit, part = gw - t * hsplit;
+  if (t >= T) return;
+  const int r =
+      token_row(t, lane, k, E, capacity, topk_idx, tile_base, slot_rank);
+  int rj[KMAX];
+  publish_rows<KMAX>(r, t, part, lane, k, row_src, tok_row, rj);
+  scatter_token_part<KMAX, MODE, U>(x, esize, H, t, part, hsplit, lane, rj,
+                                    rows, row_scales);
+}
+
+// ------------------------------------------------------------------ small batches
+
+// The routing plan of T <= kSmallPlanT tokens rebuilt in one workgroup's LDS
+// (the same results as the plan kernels): a ballot per (64-token tile,
+// expert) set by LDS atomics, counts by popcount, the exclusive scan of the
+// padded counts, and the first row of every (tile, expert).
+__device__ void local_plan(const int32_t* __restrict__ topk_idx, int T, int k,
+                           int E, int pad, unsigned long long* bits, int* base,
+                           int* cnt, int* off) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int nt = (T + 63) / 64;
+  for (int i = tid; i < nt * E; i += nthr) bits[i] = 0ull;
+  __syncthreads();
+  for (int p = tid; p < T * k; p += nthr) {
+    const int e = topk_idx[p];
+    const int t = p / k;
+    if (e >= 0 && e < E) atomicOr(&bits[(t >> 6) * E + e], 1ull << (t & 63));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nthr) {
+    int c = 0;
+    for (int q = 0; q < nt; ++q) c += __popcll(bits[q * E + e]);
+    cnt[e] = c;
+    off[e] = (c + pad - 1) / pad * pad;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive scan of the padded counts: lane l owns experts [8l, 8l+8)
+    constexpr int PER = MOE_MAX_EXPERTS / 64;
+    int loc[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid * PER + i;
+      loc[i] = e < E ? off[e] : 0;
+      sum += loc[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid * PER + i;
+      if (e < E) off[e] = run;
+      run += loc[i];
+    }
+    if (tid == 63) off[E] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nthr) {
+    int run = off[e];
+    for (int q = 0; q < nt; ++q) {
+      base[q * E + e] = run;
+      run += __popcll(bits[q * E + e]);
+    }
+  }
+  __syncthreads();
+}
+
+inline size_t local_plan_lds_bytes(int T, int E) {
+  const size_t nte = (size_t)((T + 63) / 64) * E;
+  return nte * 8 + nte * 4 + (size_t)E * 4 + (size_t)(E + 1) * 4;
+}
+
+// Plan and scatter of few tokens in one launch (the launch after the top-k):
+// every workgroup rebuilds the plan in LDS from topk_idx -- no plan kernel
+// between top-k and scatter -- then runs its share of the scatter waves or
+// of the padding fill; workgroup 0 also stores counts and offsets.
+template <int KMAX, int MODE, int U>
+__global__ __launch_bounds__(256) void plan_dispatch_small_kernel(
+    const unsigned char* __restrict__ x, int esize, int T, int H,
+    const int32_t* __restrict__ topk_idx, int k, int E, int pad,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    unsigned char* __restrict__ rows, long long capacity,
+    float* __restrict__ row_scales, int32_t* __restrict__ row_src,
+    int32_t* __restrict__ tok_row, int tok_blocks, int hsplit) {
+  extern __shared__ unsigned long long plan_lds[];
+  const int nte = ((T + 63) / 64) * E;
+  unsigned long long* bits = plan_lds;
+  int* base = reinterpret_cast<int*>(bits + nte);
+  int* cnt = base + nte;
+  int* off = cnt + E;
+  local_plan(topk_idx, T, k, E, pad, bits, base, cnt, off);
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+      if (e < E) counts[e] = cnt[e];
+      offsets[e] = off[e];
+    }
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if ((int)blockIdx.x >= tok_blocks) {
+    fill_padding_rows(blockIdx.x - tok_blocks, kDispatchFillBlocks, E, cnt,
+                      off, capacity, row_src);
+    return;
+  }
+  const int gw = blockIdx.x * 4 + wv;
+  const int t = gw / hsplit, part = gw - t * hsplit;
+  if (t >= T) return;
+  int r = -1;
+  if (lane < k) {
+    const int e = topk_idx[(size_t)t * k + lane];
+    if (e >= 0 && e < E) {
+      const int q = (t >> 6) * E + e;
+      r = base[q] + __popcll(bits[q] & ((1ull << (t & 63)) - 1ull));
+      if ((long long)r >= capacity) r = -1;
+    }
+  }
+  int rj[KMAX];
+  publish_rows<KMAX>(r, t, part, lane, k, row_src, tok_row, rj);
+  scatter_token_part<KMAX, MODE, U>(x, esize, H, t, part, hsplit, lane, rj,
+                                    rows, row_scales);
 }
 
 // ------------------------------------------------------------------ fixture
@@ -279,6 +422,30 @@ static void launch_dispatch_k(int mode, dim3 grid, hipStream_t s,
                        cap, sc, row_src, tok_row, tblocks, hs);
 }
 
+// Scatter geometry: every group of u 64-lane chunks of a token row is a wave
+// of its own (a token's waves run side by side); u = 1 when groups of two
+// chunks would leave fewer than 16384 waves (Mixtral 4096 tokens: 26 -> 22
+// us, MoonEP 8192 tokens of 768: 26.4 -> 24.5 us) or a half-empty last group
+// (DeepSeek-V3 fp8 rows of 448 chunks: 204 -> 202 us).
+struct ScatterShape {
+  int mode, esize, u, hs, tblocks;
+};
+static ScatterShape scatter_shape(int xdt, int pdt, int T, int H,
+                                  bool allow_u2 = true) {
+  ScatterShape g;
+  g.esize = xdt == DT_F32 ? 4 : 2;
+  g.mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
+  const int nch = g.mode == 0 ? H * g.esize / 16 : H / 16;  // lane chunks
+  g.u = allow_u2 && (long long)T * ((nch + 127) / 128) >= 16384 &&
+                nch % 128 == 0
+            ? 2
+            : 1;
+  g.hs = (nch + 64 * g.u - 1) / (64 * g.u);
+  g.hs = g.hs < 1 ? 1 : g.hs;
+  g.tblocks = (int)(((long long)T * g.hs + 3) / 4);
+  return g;
+}
+
 hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
                            const int32_t* topk_idx, int k, int E,
                            const int32_t* counts, const int32_t* offsets,
@@ -288,33 +455,23 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
   const int32_t* tb = (const int32_t*)workspace;
   const int32_t* sr =
       (const int32_t*)((const unsigned char*)workspace + ws_tile_bytes(T, E));
-  const int esize = xdt == DT_F32 ? 4 : 2;
-  const int mode = pdt != DT_FP8 ? 0 : (xdt == DT_BF16 ? 1 : 2);
-  // every group of U 64-lane chunks of a token row is a wave of its own
-  // (a token's waves run side by side); U = 1 when groups of two chunks
-  // would leave fewer than 16384 waves (Mixtral 4096 tokens: 26 -> 22 us,
-  // MoonEP 8192 tokens of 768: 26.4 -> 24.5 us) or a half-empty last group
-  // (DeepSeek-V3 fp8 rows of 448 chunks: 204 -> 202 us)
-  const int nch = mode == 0 ? H * esize / 16 : H / 16;   // lane chunks per row
-  const int u =
-      (long long)T * ((nch + 127) / 128) >= 16384 && nch % 128 == 0 ? 2 : 1;
-  int hs = (nch + 64 * u - 1) / (64 * u);
-  hs = hs < 1 ? 1 : hs;
-  const int tblocks = (int)(((long long)T * hs + 3) / 4);
-  const dim3 grid(tblocks + kDispatchFillBlocks);
+  const ScatterShape g = scatter_shape(xdt, pdt, T, H);
+  const dim3 grid(g.tblocks + kDispatchFillBlocks);
   const unsigned char* xb = (const unsigned char*)x;
   unsigned char* rb = (unsigned char*)rows;
   const long long cap = (long long)capacity;
 #define MOE_DISPATCH_K(KV)                                                   \
   do {                                                                       \
-    if (u == 2)                                                              \
-      launch_dispatch_k<KV, 2>(mode, grid, s, xb, esize, T, H, topk_idx, k,  \
-                               E, counts, offsets, tb, sr, rb, cap,          \
-                               row_scales, row_src, tok_row, tblocks, hs);   \
+    if (g.u == 2)                                                            \
+      launch_dispatch_k<KV, 2>(g.mode, grid, s, xb, g.esize, T, H, topk_idx, \
+                               k, E, counts, offsets, tb, sr, rb, cap,       \
+                               row_scales, row_src, tok_row, g.tblocks,      \
+                               g.hs);                                        \
     else                                                                     \
-      launch_dispatch_k<KV, 1>(mode, grid, s, xb, esize, T, H, topk_idx, k,  \
-                               E, counts, offsets, tb, sr, rb, cap,          \
-                               row_scales, row_src, tok_row, tblocks, hs);   \
+      launch_dispatch_k<KV, 1>(g.mode, grid, s, xb, g.esize, T, H, topk_idx, \
+                               k, E, counts, offsets, tb, sr, rb, cap,       \
+                               row_scales, row_src, tok_row, g.tblocks,      \
+                               g.hs);                                        \
   } while (0)
   if (k <= 1) MOE_DISPATCH_K(1);
   else if (k <= 2) MOE_DISPATCH_K(2);
@@ -322,6 +479,41 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
   else if (k <= 8) MOE_DISPATCH_K(8);
   else MOE_DISPATCH_K(16);
 #undef MOE_DISPATCH_K
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_dispatch_small(const void* x, int xdt, int T, int H,
+                                      const int32_t* topk_idx, int k, int E,
+                                      int pad, int32_t* counts,
+                                      int32_t* offsets, int pdt, void* rows,
+                                      size_t capacity, float* row_scales,
+                                      int32_t* row_src, int32_t* tok_row,
+                                      hipStream_t s) {
+  // one 64-lane chunk per lane step: few tokens spread over more waves
+  const ScatterShape g = scatter_shape(xdt, pdt, T, H, false);
+  const dim3 grid(g.tblocks + kDispatchFillBlocks);
+  const size_t lds = local_plan_lds_bytes(T, E);
+  const unsigned char* xb = (const unsigned char*)x;
+  unsigned char* rb = (unsigned char*)rows;
+  const long long cap = (long long)capacity;
+#define MOE_PDS(KV, MV, UV)                                                   \
+  hipLaunchKernelGGL((plan_dispatch_small_kernel<KV, MV, UV>), grid,          \
+                     dim3(256), lds, s, xb, g.esize, T, H, topk_idx, k, E,    \
+                     pad, counts, offsets, rb, cap, row_scales, row_src,      \
+                     tok_row, g.tblocks, g.hs)
+#define MOE_PDS_M(KV)                                                         \
+  do {                                                                        \
+    if (g.mode == 0) MOE_PDS(KV, 0, 1);                                       \
+    else if (g.mode == 1) MOE_PDS(KV, 1, 1);                                  \
+    else MOE_PDS(KV, 2, 1);                                                   \
+  } while (0)
+  if (k <= 1) MOE_PDS_M(1);
+  else if (k <= 2) MOE_PDS_M(2);
+  else if (k <= 4) MOE_PDS_M(4);
+  else if (k <= 8) MOE_PDS_M(8);
+  else MOE_PDS_M(16);
+#undef MOE_PDS_M
+#undef MOE_PDS
   return hipGetLastError();
 }
 

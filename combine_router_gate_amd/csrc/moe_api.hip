@@ -236,6 +236,62 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
       (hipStream_t)stream));
 }
 
+int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
+                       const void* w_gate, int E, const float* bias, int k,
+                       int pad, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* offsets, float* logits_dbg,
+                       void* workspace, size_t workspace_bytes,
+                       int payload_dtype, void* rows, size_t rows_capacity,
+                       float* row_scales, int32_t* row_src, int32_t* tok_row,
+                       void* stream) {
+  int st = check_route_shape(T, E, k, pad);
+  if (st != MOE_OK) return st;
+  if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  const bool fp8 = payload_dtype == MOE_FP8_E4M3;
+  if (payload_dtype != x_dtype && !fp8) return MOE_ERR_DTYPE;
+  if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;
+  if (counts == nullptr || offsets == nullptr || row_src == nullptr)
+    return MOE_ERR_NULL;
+  if (fp8 != (row_scales != nullptr)) return fp8 ? MOE_ERR_NULL : MOE_ERR_DTYPE;
+  if (T > 0 && (x == nullptr || w_gate == nullptr || topk_idx == nullptr ||
+                topk_w == nullptr || workspace == nullptr || rows == nullptr ||
+                tok_row == nullptr))
+    return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(bias, 4) ||
+      !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) ||
+      !aligned(offsets, 4) || !aligned(logits_dbg, 4) ||
+      !aligned(workspace, 16) || !aligned(rows, 16) ||
+      !aligned(row_scales, 4) || !aligned(row_src, 4) || !aligned(tok_row, 4))
+    return MOE_ERR_ALIGN;
+  if (rows_capacity < moe_rows_capacity(T, E, k, pad)) return MOE_ERR_CAPACITY;
+  if (rows_capacity > 0x7fffffffULL) return MOE_ERR_SHAPE;
+  if (workspace_bytes < moe::workspace_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+  const size_t es = dtype_size(x_dtype), ps = dtype_size(payload_dtype);
+  const Span ins[] = {{x, (size_t)T * H * es}, {w_gate, (size_t)E * H * es},
+                      {bias, bias ? (size_t)E * 4 : 0}};
+  const Span outs[] = {{topk_idx, (size_t)T * k * 4},
+                       {topk_w, (size_t)T * k * 4},
+                       {counts, (size_t)E * 4},
+                       {offsets, (size_t)(E + 1) * 4},
+                       {logits_dbg, logits_dbg ? (size_t)T * E * 4 : 0},
+                       {workspace, moe::workspace_bytes(T, E, k)},
+                       {rows, rows_capacity * H * ps},
+                       {row_scales, fp8 ? rows_capacity * (H / 128) * 4 : 0},
+                       {row_src, rows_capacity * 4},
+                       {tok_row, (size_t)T * k * 4}};
+  if (any_overlap(outs, 10, ins, 3)) return MOE_ERR_ALIAS;
+  if (trace_on())
+    std::fprintf(stderr,
+                 "moe_route_dispatch T=%d H=%d E=%d k=%d pad=%d dtype=%d "
+                 "payload=%d cap=%zu\n",
+                 T, H, E, k, pad, x_dtype, payload_dtype, rows_capacity);
+  return hip_status(moe::launch_route_dispatch(
+      x, w_gate, x_dtype, bias, T, H, E, k, pad, topk_idx, topk_w, counts,
+      offsets, logits_dbg, workspace, payload_dtype, rows, rows_capacity,
+      row_scales, row_src, tok_row, (hipStream_t)stream));
+}
+
 size_t moe_noalloc_scratch_bytes(int T, int E, int k) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK)
     return 0;

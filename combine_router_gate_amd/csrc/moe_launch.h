@@ -83,6 +83,27 @@ hipError_t launch_dispatch(const void* x, int xdt, int T, int H,
                            size_t capacity, float* row_scales,
                            int32_t* row_src, int32_t* tok_row, hipStream_t s);
 
+// Plan and scatter of T <= kSmallPlanT tokens in one launch (each workgroup
+// rebuilds the plan in LDS from topk_idx; counts and offsets are written)
+hipError_t launch_plan_dispatch_small(const void* x, int xdt, int T, int H,
+                                      const int32_t* topk_idx, int k, int E,
+                                      int pad, int32_t* counts,
+                                      int32_t* offsets, int pdt, void* rows,
+                                      size_t capacity, float* row_scales,
+                                      int32_t* row_src, int32_t* tok_row,
+                                      hipStream_t s);
+
+// moe_route followed by moe_dispatch; few tokens without a plan kernel
+hipError_t launch_route_dispatch(const void* x, const void* w, int xdt,
+                                 const float* bias, int T, int H, int E,
+                                 int k, int pad, int32_t* topk_idx,
+                                 float* topk_w, int32_t* counts,
+                                 int32_t* offsets, float* logits_dbg,
+                                 void* workspace, int pdt, void* rows,
+                                 size_t capacity, float* row_scales,
+                                 int32_t* row_src, int32_t* tok_row,
+                                 hipStream_t s);
+
 // moe_dispatch with its tile plan rebuilt in the library's static scratch
 hipError_t launch_dispatch_noalloc(const void* x, int xdt, int T, int H,
                                    const int32_t* topk_idx, int k, int E,

@@ -1468,6 +1468,25 @@ static hipError_t launch_scan(int32_t* tile_base, int nt, int E, int pad,
   return hipGetLastError();
 }
 
+// The gate kernels of moe_route; *stage says what remains (plan or scan).
+static hipError_t launch_gate(const void* x, const void* w, int xdt,
+                              const float* bias, int T, int H, int E, int k,
+                              int32_t* topk_idx, float* topk_w,
+                              float* logits_dbg, void* workspace, int* stage,
+                              hipStream_t s) {
+  int32_t* tile_base = (int32_t*)workspace;
+  int32_t* slot_rank =
+      (int32_t*)((unsigned char*)workspace + ws_tile_bytes(T, E));
+  *stage = kRouteNeedPlan;
+  if (xdt == DT_BF16)
+    return launch_gate_typed<uint16_t>(
+        (const uint16_t*)x, (const uint16_t*)w, bias, T, H, E, k, topk_idx,
+        topk_w, logits_dbg, tile_base, slot_rank, stage, s);
+  return launch_gate_typed<float>((const float*)x, (const float*)w, bias, T,
+                                  H, E, k, topk_idx, topk_w, logits_dbg,
+                                  tile_base, slot_rank, stage, s);
+}
+
 hipError_t launch_route(const void* x, const void* w, int xdt,
                         const float* bias, int T, int H, int E, int k,
                         int pad, int32_t* topk_idx, float* topk_w,
@@ -1475,24 +1494,50 @@ hipError_t launch_route(const void* x, const void* w, int xdt,
                         void* workspace, hipStream_t s) {
   if (T == 0)
     return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
-  int32_t* tile_base = (int32_t*)workspace;
-  int32_t* slot_rank =
-      (int32_t*)((unsigned char*)workspace + ws_tile_bytes(T, E));
   int stage = kRouteNeedPlan;
-  hipError_t err;
-  if (xdt == DT_BF16)
-    err = launch_gate_typed<uint16_t>((const uint16_t*)x, (const uint16_t*)w,
-                                      bias, T, H, E, k, topk_idx, topk_w,
-                                      logits_dbg, tile_base, slot_rank, &stage,
-                                      s);
-  else
-    err = launch_gate_typed<float>((const float*)x, (const float*)w, bias, T,
-                                   H, E, k, topk_idx, topk_w, logits_dbg,
-                                   tile_base, slot_rank, &stage, s);
+  hipError_t err = launch_gate(x, w, xdt, bias, T, H, E, k, topk_idx, topk_w,
+                               logits_dbg, workspace, &stage, s);
   if (err != hipSuccess) return err;
   if (stage == kRouteNeedPlan)
     return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
-  return launch_scan(tile_base, num_tiles(T), E, pad, counts, offsets, s);
+  return launch_scan((int32_t*)workspace, num_tiles(T), E, pad, counts,
+                     offsets, s);
+}
+
+// moe_route then moe_dispatch.  When the top-k leaves the plan to do for at
+// most kSmallPlanT tokens, the plan kernel is skipped: the scatter launch
+// rebuilds the plan in every workgroup (one launch fewer on the decode
+// path); otherwise the two calls' launches as they are.
+hipError_t launch_route_dispatch(const void* x, const void* w, int xdt,
+                                 const float* bias, int T, int H, int E,
+                                 int k, int pad, int32_t* topk_idx,
+                                 float* topk_w, int32_t* counts,
+                                 int32_t* offsets, float* logits_dbg,
+                                 void* workspace, int pdt, void* rows,
+                                 size_t capacity, float* row_scales,
+                                 int32_t* row_src, int32_t* tok_row,
+                                 hipStream_t s) {
+  hipError_t err;
+  if (T > 0 && T <= kSmallPlanT) {
+    int stage = kRouteNeedPlan;
+    err = launch_gate(x, w, xdt, bias, T, H, E, k, topk_idx, topk_w,
+                      logits_dbg, workspace, &stage, s);
+    if (err != hipSuccess) return err;
+    if (stage == kRouteNeedPlan)
+      return launch_plan_dispatch_small(x, xdt, T, H, topk_idx, k, E, pad,
+                                        counts, offsets, pdt, rows, capacity,
+                                        row_scales, row_src, tok_row, s);
+    err = launch_scan((int32_t*)workspace, num_tiles(T), E, pad, counts,
+                      offsets, s);
+  } else {
+    err = launch_route(x, w, xdt, bias, T, H, E, k, pad, topk_idx, topk_w,
+                       counts, offsets, logits_dbg, workspace, s);
+  }
+  if (err != hipSuccess) return err;
+  if (T == 0 && capacity == 0) return hipSuccess;
+  return launch_dispatch(x, xdt, T, H, topk_idx, k, E, counts, offsets,
+                         workspace, pdt, rows, capacity, row_scales, row_src,
+                         tok_row, s);
 }
 
 hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,

@@ -6,9 +6,11 @@ current HIP stream.  There is no fallback: if the library is not built this
 module raises on first use.
 
 Low-level functions carry the C names (``moe_route``, ``moe_plan``,
-``moe_dispatch``, ``moe_dispatch_noalloc``, ``moe_combine_residual``, ``moe_farskip_aux``,
+``moe_dispatch``, ``moe_route_dispatch``, ``moe_dispatch_noalloc``,
+``moe_combine_residual``, ``moe_farskip_aux``,
 ``moe_combine_backward``, ``moe_dispatch_backward``, ``moe_expert_gemm_fp8``,
-``moe_expert_fixture``) and take preallocated tensors; ``route`` / ``plan`` /
+``moe_expert_fixture``) and take preallocated tensors; ``route`` /
+``route_dispatch`` / ``plan`` /
 ``dispatch`` / ``combine_residual`` / ``farskip_aux`` /
 ``combine_main_residual`` / ``combine_backward`` / ``dispatch_backward`` /
 ``expert_gemm_fp8`` / ``expert_fixture`` allocate their outputs with torch
@@ -43,6 +45,9 @@ _SIGS = {
     "moe_plan": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "moe_dispatch": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp,
                           _sz, _i, _vp, _sz, _vp, _vp, _vp, _vp]),
+    "moe_route_dispatch": (_i, [_vp, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp,
+                                _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp, _sz,
+                                _vp, _vp, _vp, _vp]),
     "moe_noalloc_scratch_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch_noalloc": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp,
                                   _i, _vp, _sz, _vp, _vp, _vp, _vp]),
@@ -173,6 +178,21 @@ def moe_dispatch(x, topk_idx, E, pad, counts, offsets, workspace,
     _check(st, "moe_dispatch")
 
 
+def moe_route_dispatch(x, w_gate, bias, k, pad, topk_idx, topk_w, counts,
+                       offsets, logits_dbg, workspace, payload_dtype, rows,
+                       row_scales, row_src, tok_row, stream=None):
+    T, H = x.shape
+    E = w_gate.shape[0]
+    st = lib().moe_route_dispatch(
+        _ptr(x), _dt(x), T, H, _ptr(w_gate), E, _ptr(bias), k, pad,
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+        _ptr(logits_dbg), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, payload_dtype,
+        _ptr(rows), rows.shape[0], _ptr(row_scales), _ptr(row_src),
+        _ptr(tok_row), stream if stream is not None else _stream(x.device))
+    _check(st, "moe_route_dispatch")
+
+
 def moe_noalloc_scratch_bytes(T: int, E: int, k: int) -> int:
     return lib().moe_noalloc_scratch_bytes(T, E, k)
 
@@ -282,6 +302,44 @@ def route(x: torch.Tensor, w_gate: torch.Tensor, k: int, pad: int,
               p["counts"], p["offsets"], p["logits"], p["workspace"])
     p.update(E=E, k=k, pad=pad, T=T)
     return p
+
+
+def route_dispatch(x: torch.Tensor, w_gate: torch.Tensor, k: int, pad: int,
+                   bias: Optional[torch.Tensor] = None, payload: str = "same",
+                   want_logits: bool = False):
+    """moe_route + moe_dispatch in one call (small batches skip the plan
+    kernel).  Returns (plan, dispatched) like route() and dispatch()."""
+    T, H = x.shape
+    E = w_gate.shape[0]
+    dev = x.device
+    p = dict(
+        topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        workspace=torch.empty(max(moe_workspace_bytes(T, E, k), 1),
+                              dtype=torch.uint8, device=dev),
+        logits=(torch.empty((T, E), dtype=torch.float32, device=dev)
+                if want_logits else None),
+    )
+    p.update(E=E, k=k, pad=pad, T=T)
+    cap = moe_rows_capacity(T, E, k, pad)
+    fp8 = payload == "fp8"
+    pdt = MOE_FP8_E4M3 if fp8 else _dt(x)
+    d = dict(
+        rows=torch.empty((cap, H), dtype=torch.uint8 if fp8 else x.dtype,
+                         device=dev),
+        row_scales=(torch.empty((cap, H // 128), dtype=torch.float32,
+                                device=dev) if fp8 else None),
+        row_src=torch.empty(cap, dtype=torch.int32, device=dev),
+        tok_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+        payload_dtype=pdt,
+    )
+    moe_route_dispatch(x, w_gate, bias, k, pad, p["topk_idx"], p["topk_w"],
+                       p["counts"], p["offsets"], p["logits"], p["workspace"],
+                       pdt, d["rows"], d["row_scales"], d["row_src"],
+                       d["tok_row"])
+    return p, d
 
 
 def plan(topk_idx: torch.Tensor, E: int, pad: int) -> Dict[str, torch.Tensor]:

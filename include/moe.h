@@ -11,7 +11,9 @@
  *   moe_dispatch         stable scatter of token rows into an expert-major
  *                        buffer padded per expert (optionally OCP fp8 E4M3
  *                        with one fp32 scale per 1x128 block)
- *   moe_dispatch_noalloc the same with no workspace argument (its scratch is
+ *   moe_route_dispatch   moe_route + moe_dispatch in one call (small decode
+ *                        batches skip the plan kernel)
+ *   moe_dispatch_noalloc moe_dispatch with no workspace argument (its scratch is
  *                        a static device array), for callers that cannot
  *                        allocate
  *   moe_combine_residual weighted gather-combine back to token order, fused
@@ -205,6 +207,32 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
                  void* rows, size_t rows_capacity, float* row_scales,
                  int32_t* row_src, int32_t* tok_row,
                  void* stream);
+
+/*
+ * moe_route_dispatch -- moe_route followed by moe_dispatch in one call, for
+ * the low-latency path of small decode batches (DeepEP's low-latency kernels
+ * for small decode batches: DeepEP release news, technical overview).  The
+ * arguments are the union of the two calls' (same meaning, layout and
+ * limits); the outputs are bit-identical to moe_route then moe_dispatch on
+ * the same stream.  Up to 512 tokens the plan kernel between top-k and
+ * scatter is skipped: every scatter workgroup rebuilds the plan (tile
+ * ballots, counts, padded scan) in its own LDS from topk_idx, so route +
+ * scatter take one launch fewer (a grid-wide barrier inside one kernel
+ * measured slower on this GPU than the kernel boundary it would replace).
+ * The workspace is then scratch of this call only: it does not hold a plan
+ * a later moe_dispatch could read.  Errors as for the two calls.
+ */
+int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
+                       const void* w_gate, int E, const float* bias,
+                       int k, int pad,
+                       int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* offsets,
+                       float* logits_dbg,
+                       void* workspace, size_t workspace_bytes,
+                       int payload_dtype,
+                       void* rows, size_t rows_capacity, float* row_scales,
+                       int32_t* row_src, int32_t* tok_row,
+                       void* stream);
 
 /*
  * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate

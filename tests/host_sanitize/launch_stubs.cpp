@@ -37,6 +37,22 @@ hipError_t launch_dispatch_noalloc(const void*, int, int, int,
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_route_dispatch(const void*, const void*, int, const float*,
+                                 int, int, int, int, int, int32_t*, float*,
+                                 int32_t*, int32_t*, float*, void*, int,
+                                 void*, size_t, float*, int32_t*, int32_t*,
+                                 hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_plan_dispatch_small(const void*, int, int, int,
+                                      const int32_t*, int, int, int,
+                                      int32_t*, int32_t*, int, void*, size_t,
+                                      float*, int32_t*, int32_t*,
+                                      hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_combine(const void*, int, int, size_t, const int32_t*,
                           const float*, int, int, const void*, const void*,
                           void*, void*, void*, int, hipStream_t) {

@@ -121,6 +121,28 @@ int main() {
        dna(300000, 16, 8, moe_rows_capacity(300000, 16, 8, 4)));
   CASE("noalloc cap", MOE_ERR_CAPACITY, dna(100, 16, 2, cap - 1));
 
+  auto rd = [&](int T, int H, int pdt, float* sc, size_t cap_, void* ws,
+                void* rows) {
+    return moe_route_dispatch(P(0), MOE_BF16, T, H, P(1), 16, nullptr, 2, 4,
+                              Q<int32_t>(2), Q<float>(3), Q<int32_t>(4),
+                              Q<int32_t>(5), nullptr, ws,
+                              moe_workspace_bytes(T > 0 ? T : 1, 16, 2), pdt,
+                              rows, cap_, sc, Q<int32_t>(8), Q<int32_t>(9),
+                              nullptr);
+  };
+  CASE("route_dispatch ok", MOE_OK,
+       rd(100, 256, MOE_BF16, nullptr, cap, P(6), P(7)));
+  CASE("route_dispatch fp8 ok", MOE_OK,
+       rd(100, 256, MOE_FP8_E4M3, Q<float>(10), cap, P(6), P(7)));
+  CASE("route_dispatch cap", MOE_ERR_CAPACITY,
+       rd(100, 256, MOE_BF16, nullptr, cap - 1, P(6), P(7)));
+  CASE("route_dispatch alias rows/ws", MOE_ERR_ALIAS,
+       rd(100, 256, MOE_BF16, nullptr, cap, P(6), P(6)));
+  CASE("route_dispatch alias rows/x", MOE_ERR_ALIAS,
+       rd(100, 256, MOE_BF16, nullptr, cap, P(6), P(0)));
+  CASE("route_dispatch INT_MAX", MOE_ERR_SHAPE,
+       rd(INT_MAX, 256, MOE_BF16, nullptr, cap, P(6), P(7)));
+
   // ---------------------------------------------------------- combine
   auto comb = [&](int T, int H, size_t y_rows, void* res_in, void* res_out,
                   void* rnr, void* out) {

@@ -140,6 +140,35 @@ def test_dispatch_validation(L, no_gpu, kw, want):
     assert _dispatch(L, **kw) == want
 
 
+def _route_dispatch(L, **kw):
+    a = dict(x=A[0], xdt=1, T=100, H=256, w=A[1], E=16, bias=None, k=2, pad=4,
+             idx=A[2], tw=A[3], counts=A[4], offsets=A[5], dbg=None, ws=A[6],
+             wsb=1 << 26, pdt=1, rows=A[7],
+             cap=O.rows_capacity(100, 16, 2, 4), scales=None, row_src=A[8],
+             tok_row=A[9], stream=None)
+    a.update(kw)
+    return L.moe_route_dispatch(
+        a["x"], a["xdt"], a["T"], a["H"], a["w"], a["E"], a["bias"], a["k"],
+        a["pad"], a["idx"], a["tw"], a["counts"], a["offsets"], a["dbg"],
+        a["ws"], a["wsb"], a["pdt"], a["rows"], a["cap"], a["scales"],
+        a["row_src"], a["tok_row"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(rows=None), NULL),
+    (dict(ws=None), NULL), (dict(row_src=None), NULL), (dict(pdt=2), NULL),
+    (dict(scales=A[10]), DTYPE), (dict(xdt=2), DTYPE), (dict(pdt=0), DTYPE),
+    (dict(pdt=2, scales=A[10], H=200), SHAPE), (dict(k=17), SHAPE),
+    (dict(E=513), SHAPE), (dict(H=12), SHAPE),
+    (dict(cap=O.rows_capacity(100, 16, 2, 4) - 1), CAP), (dict(wsb=10), WS),
+    (dict(rows=A[7] + 4), ALIGN), (dict(ws=A[6] + 8), ALIGN),
+    (dict(rows=A[0]), ALIAS), (dict(rows=A[6]), ALIAS),
+    (dict(tok_row=A[2]), ALIAS), (dict(row_src=A[1]), ALIAS),
+])
+def test_route_dispatch_validation(L, no_gpu, kw, want):
+    assert _route_dispatch(L, **kw) == want
+
+
 def _dispatch_noalloc(L, **kw):
     a = dict(x=A[0], xdt=1, T=100, H=256, idx=A[1], k=2, E=16, pad=4,
              counts=A[2], offsets=A[3], pdt=1, rows=A[5],

@@ -1,0 +1,131 @@
+"""moe_route_dispatch (route + scatter in one call; up to 512 tokens the
+scatter launch rebuilds the plan in every workgroup instead of a plan kernel)
+through the C ABI: every output bit-identical to moe_route followed by
+moe_dispatch, and checked against the oracle -- the exact plan on integer
+inputs, top-k against the kernel's own logits and plan validity otherwise,
+sampled payload rows everywhere."""
+import numpy as np
+import pytest
+import torch
+
+from combine_router_gate_amd import inputs as I
+from combine_router_gate_amd import moe
+from oracle import moe_oracle as O
+from _gpu_common import (LOGIT_TOL, check_plan_valid, check_topk_own_logits,
+                         note, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+C = I.CONFIGS
+CASES = {
+    # small split gate (reduction one token per workgroup), fused plan
+    "decode": C["dsv3_decode"],
+    "decode_fp8": C["dsv3_decode"].with_shape(payload="fp8"),
+    "t1": C["dsv3_decode"].with_shape(T=1, H=2048),
+    "t512_e512_k16": C["moonep_skew"].with_shape(T=512, H=512, E=512, k=16,
+                                                 pad=8, zipf_bias=False),
+    "moonep_bias_t200": C["moonep_skew"].with_shape(T=200),
+    # fp32 gates (k-split, wide) then the fused plan
+    "f32_e20": C["tiny"].with_shape(T=99, H=64, E=20, k=3, pad=2),
+    "f32_e100_fp8": C["tiny"].with_shape(T=130, H=256, E=100, k=4, pad=3,
+                                         payload="fp8", y_dtype="bf16"),
+    "tiny": C["tiny"],
+    # one-pass gate (its epilogue writes the tile plan: scan, then dispatch)
+    "onepass_h64": C["moonep_skew"].with_shape(T=100, H=64, E=512, k=16,
+                                               pad=8, zipf_bias=False),
+    # beyond 512 tokens: the two calls' launches
+    "t513": C["dsv3_decode"].with_shape(T=513, H=512),
+}
+
+
+def _separate(x, w, b, cfg):
+    p = moe.route(x, w, cfg.k, cfg.pad, bias=b, want_logits=True)
+    d = moe.dispatch(x, p, payload="fp8" if cfg.payload == "fp8" else "same")
+    return p, d
+
+
+def _compare_to_separate(p, d, p2, d2, cfg):
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "logits"):
+        assert np.array_equal(to_host(p[key]).view(np.uint32),
+                              to_host(p2[key]).view(np.uint32)), key
+    for key in ("row_src", "tok_row"):
+        assert np.array_equal(to_host(d[key]), to_host(d2[key])), key
+    valid = torch.from_numpy(np.nonzero(to_host(d["row_src"]) >= 0)[0]).cuda()
+    assert np.array_equal(to_host(d["rows"][valid]).view(np.uint8),
+                          to_host(d2["rows"][valid]).view(np.uint8)), "rows"
+    if cfg.payload == "fp8":
+        assert np.array_equal(to_host(d["row_scales"][valid]),
+                              to_host(d2["row_scales"][valid])), "scales"
+
+
+def _sampled_rows(wl, d, cfg, n=64, seed=0):
+    row_src = to_host(d["row_src"])
+    valid = np.nonzero(row_src >= 0)[0]
+    rsel = np.random.default_rng(seed).choice(valid, min(n, len(valid)),
+                                              replace=False)
+    ridx = torch.from_numpy(rsel.astype(np.int64)).cuda()
+    g_rows = to_host(d["rows"][ridx])
+    g_sc = to_host(d["row_scales"][ridx]) if cfg.payload == "fp8" else None
+    for i, r in enumerate(rsel):
+        pay, sc = O.dispatch_row(wl.x.values[row_src[r]], cfg.payload)
+        assert np.array_equal(g_rows[i], pay), f"row {r}"
+        if g_sc is not None:
+            assert np.array_equal(g_sc[i], sc), f"scales of row {r}"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_dispatch_matches_calls_and_oracle(name):
+    cfg = CASES[name]
+    note(f"route_dispatch {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} "
+         f"x={cfg.x_dtype} payload={cfg.payload}")
+    wl = I.make_workload(cfg, 5)
+    x, w = to_dev(wl.x), to_dev(wl.w_gate)
+    b = to_dev(wl.bias) if wl.bias is not None else None
+    p, d = moe.route_dispatch(x, w, cfg.k, cfg.pad, bias=b,
+                              payload="fp8" if cfg.payload == "fp8"
+                              else "same", want_logits=True)
+    p2, d2 = _separate(x, w, b, cfg)
+    torch.cuda.synchronize()
+    _compare_to_separate(p, d, p2, d2, cfg)
+    o = O.route(wl.x.values, wl.w_gate.values, wl.bias, cfg.k, cfg.pad)
+    gl = to_host(p["logits"])
+    assert np.abs(gl.astype(np.float64) - o["logits"]).max() <= LOGIT_TOL
+    gi = to_host(p["topk_idx"])
+    check_topk_own_logits(gi, to_host(p["topk_w"]), gl, cfg.k)
+    check_plan_valid(gi, to_host(p["counts"]), to_host(p["offsets"]),
+                     to_host(d["tok_row"]), to_host(d["row_src"]), cfg.E,
+                     cfg.pad)
+    _sampled_rows(wl, d, cfg)
+
+
+@pytest.mark.parametrize("name", ["decode", "t512_e512_k16", "f32_e20"])
+def test_route_dispatch_integer_inputs_equal_oracle_plan(name):
+    """Exact logits: the routing and the whole plan equal the oracle's."""
+    cfg = CASES[name]
+    note(f"route_dispatch integer {name}")
+    wl = I.integer_workload(cfg, 3)
+    x, w = to_dev(wl.x), to_dev(wl.w_gate)
+    p, d = moe.route_dispatch(x, w, cfg.k, cfg.pad,
+                              payload="fp8" if cfg.payload == "fp8"
+                              else "same")
+    torch.cuda.synchronize()
+    o = O.route(wl.x.values, wl.w_gate.values, None, cfg.k, cfg.pad)
+    assert np.array_equal(to_host(p["topk_idx"]), o["topk_idx"])
+    assert np.array_equal(to_host(p["counts"]), o["counts"])
+    assert np.array_equal(to_host(p["offsets"]), o["offsets"])
+    cap = O.rows_capacity(cfg.T, cfg.E, cfg.k, cfg.pad)
+    o_tok, o_src = O.assign_slots(o["topk_idx"], o["offsets"], cfg.E, cap)
+    assert np.array_equal(to_host(d["tok_row"]), o_tok)
+    assert np.array_equal(to_host(d["row_src"]), o_src)
+    _sampled_rows(wl, d, cfg, n=256)
+
+
+def test_route_dispatch_no_tokens():
+    cfg = C["dsv3_decode"].with_shape(T=0, H=256, E=64, k=4, pad=8)
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((cfg.E, cfg.H), dtype=torch.bfloat16, device="cuda")
+    p, d = moe.route_dispatch(x, w, cfg.k, cfg.pad)
+    torch.cuda.synchronize()
+    assert (to_host(p["counts"]) == 0).all()
+    assert (to_host(p["offsets"]) == 0).all()
+    assert (to_host(d["row_src"]) == -1).all()
