@@ -21,6 +21,9 @@ inline int num_tiles(int T) { return (int)(((long long)T + 63) / 64); }
 //                                dimension is split S ways (up to
 //                                kSplitMaxT tokens); S <= split_max(T), EP =
 //                                experts padded to the gate's 64 * EPW
+//   group     [G, E] int32       per-group expert totals of the parallel
+//                                scan (G = ceil(tiles / 16), up to
+//                                kSplitMaxT tokens)
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 constexpr int kSplitRows = 16384;
 constexpr int kSplitMax = 64;
@@ -49,10 +52,23 @@ inline size_t ws_partial_bytes(int T, int E) {
 }
 // Up to this many tokens, histogram, scan and ranks run in one workgroup.
 constexpr int kSmallPlanT = 512;
+// Tiles per group of the parallel scan: the histogram producers of a split
+// gate add each tile's expert counts into its group's totals
+// [ceil(tiles / kScanGroup), E] int32 (zeroed by the gate kernel of the
+// same call), so one scan workgroup per group needs no other group's tiles.
+constexpr int kScanGroup = 16;
+inline int num_groups(int T) {
+  return (num_tiles(T) + kScanGroup - 1) / kScanGroup;
+}
+inline size_t ws_group_bytes(int T, int E) {
+  return T > 0 && T <= kSplitMaxT
+             ? align256(size_t(num_groups(T)) * size_t(E) * 4)
+             : 0;
+}
 inline size_t workspace_bytes(int T, int E, int k) {
   return T == 0 ? 0
                 : ws_tile_bytes(T, E) + ws_rank_bytes(T, k) +
-                      ws_partial_bytes(T, E);
+                      ws_partial_bytes(T, E) + ws_group_bytes(T, E);
 }
 
 // Bytes of the static scratch moe_dispatch_noalloc uses: the workspace's

@@ -104,6 +104,21 @@ __device__ __forceinline__ int gate_lds_swz(int r) {
   return (r & 7) ^ ((r >> 3) & 1);
 }
 
+// The histogram producers after a split gate accumulate per-group expert
+// totals with integer atomics; the gate kernel, which runs first in the same
+// call, clears them (n ints, spread over every thread of the grid).
+__device__ __forceinline__ void clear_group_totals(int32_t* __restrict__ g,
+                                                   int n) {
+  if (g == nullptr) return;
+  const long long bid = blockIdx.x + (long long)gridDim.x *
+                                         (blockIdx.y + (long long)gridDim.y *
+                                                           blockIdx.z);
+  const long long nthr =
+      (long long)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+  for (long long i = bid * blockDim.x + threadIdx.x; i < n; i += nthr)
+    g[i] = 0;
+}
+
 // ------------------------------------------------------------------ top-k
 
 // Top-k of one token per 16-lane group.  Lane c of the group holds the
@@ -483,7 +498,9 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
 template <int EPW, int TT, int PQ, int D, int DX = D>
 __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, int eps, float* __restrict__ partial) {
+    int H, int E, int KR, int eps, float* __restrict__ partial,
+    int32_t* __restrict__ gzero, int gzero_n) {
+  clear_group_totals(gzero, gzero_n);
   const int e0 = blockIdx.z * 64 * EPW;    // first expert of the group
   constexpr int TTOK = 16 * TT;            // tokens of the workgroup
   constexpr int KS = 32 * PQ;              // k per super-step
@@ -621,7 +638,9 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
 template <int EPW, int TT>
 __global__ __launch_bounds__(512, 1) void gate_partial_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, int tiles, int xg, float* __restrict__ partial) {
+    int H, int E, int KR, int tiles, int xg, float* __restrict__ partial,
+    int32_t* __restrict__ gzero, int gzero_n) {
+  clear_group_totals(gzero, gzero_n);
   // One-dimensional grid of tiles * S workgroups; workgroup i runs on XCD
   // i % 8.  With xg = 8 / S (S dividing 8, tiles a multiple of xg) every XCD
   // serves one hidden range, so its L2 holds 1/S of the gate weight;
@@ -764,7 +783,8 @@ __global__ __launch_bounds__(64 * WAVES) void gate_reduce_quad_kernel(
     const float* __restrict__ partial, int S, int T, int E, int k,
     const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits_dbg,
-    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank) {
+    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank,
+    int32_t* __restrict__ gtot) {
   constexpr int EP = 64 * EPW, ET = 4 * EPW;
   constexpr int NT = 64 * WAVES, TOK = 4 * WAVES;
   constexpr bool HIST = TOK == 64;
@@ -835,8 +855,12 @@ __global__ __launch_bounds__(64 * WAVES) void gate_reduce_quad_kernel(
     topk_select_write<ET, true>(v, t, T, E, k, topk_idx, topk_w);
   if constexpr (HIST) {
     __syncthreads();
-    for (int e = tid; e < E; e += NT)
-      tile_base[(size_t)blockIdx.x * E + e] = __popcll(tile_bits[e]);
+    for (int e = tid; e < E; e += NT) {
+      const int c = __popcll(tile_bits[e]);
+      tile_base[(size_t)blockIdx.x * E + e] = c;
+      if (gtot != nullptr && c != 0)
+        atomicAdd(&gtot[(size_t)(blockIdx.x / kScanGroup) * E + e], c);
+    }
     const int n = min(64, T - t0) * k;
     for (int q = tid; q < n; q += NT) {
       const int tq = q / k, j = q - tq * k;
@@ -916,9 +940,12 @@ __global__ __launch_bounds__(256) void gate_topk_ksplit_kernel(
 
 // One workgroup per 64-token tile.  bits[e] has bit i set iff token t0+i
 // chose expert e: the tile's "ballot" for e, assembled in LDS.
+// With gtot, each tile's counts are also added to its group's totals (the
+// parallel scan's input; cleared earlier in the same call).
 __global__ __launch_bounds__(256) void tile_histogram_kernel(
     const int32_t* __restrict__ topk_idx, int T, int k, int E,
-    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank) {
+    int32_t* __restrict__ tile_base, int32_t* __restrict__ slot_rank,
+    int32_t* __restrict__ gtot) {
   __shared__ unsigned long long bits[MOE_MAX_EXPERTS];
   const int tile = blockIdx.x;
   const int t0 = tile * kTileT;
@@ -932,8 +959,12 @@ __global__ __launch_bounds__(256) void tile_histogram_kernel(
     if (e >= 0 && e < E) atomicOr(&bits[e], 1ull << (p / k));
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256)
-    tile_base[(size_t)tile * E + e] = __popcll(bits[e]);
+  for (int e = tid; e < E; e += 256) {
+    const int c = __popcll(bits[e]);
+    tile_base[(size_t)tile * E + e] = c;
+    if (gtot != nullptr && c != 0)
+      atomicAdd(&gtot[(size_t)(tile / kScanGroup) * E + e], c);
+  }
   for (int p = tid; p < n; p += 256) {
     const int e = ids[p];
     const int tl = p / k;
@@ -1023,6 +1054,111 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
           tile_base[(size_t)(b0 + u) * E + e] = run;
           run += v[u];
         }
+      }
+    }
+  }
+}
+
+// Parallel form of the scan, one workgroup per group of kScanGroup tiles,
+// from the per-group expert totals the histogram producers accumulated:
+// every workgroup adds the totals of all groups (experts' counts) and of the
+// groups before its own, scans the padded counts over the experts (the
+// offsets; workgroup 0 stores counts and offsets) and turns its tiles'
+// counts into first rows.  No workgroup reads another group's tiles.
+__global__ __launch_bounds__(256) void expert_scan_groups_kernel(
+    int32_t* __restrict__ tile_base, int ntiles, int E, int pad,
+    const int32_t* __restrict__ gtot, int ngroups,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  constexpr int PER = MOE_MAX_EXPERTS / 256;   // experts per thread
+  constexpr int B = 16;                        // loads in flight
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  int tot[PER], pre[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    tot[i] = 0;
+    pre[i] = 0;
+  }
+  // thread tid owns experts tid * PER + i (consecutive, for the scan)
+  for (int q0 = 0; q0 < ngroups; q0 += B) {
+    int v[B][PER];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int q = min(q0 + b, ngroups - 1);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid * PER + i;
+        v[b][i] = gtot[(size_t)q * E + (e < E ? e : E - 1)];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int q = q0 + b;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (q < ngroups) tot[i] += v[b][i];
+        if (q < g) pre[i] += v[b][i];
+      }
+    }
+  }
+  int padded[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
+    padded[i] = e < E ? (tot[i] + pad - 1) / pad * pad : 0;
+    sum += padded[i];
+  }
+  // exclusive scan of the thread sums: within each wave, then the 4 waves
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int q = 0; q < wv; ++q) run += wsum[q];
+  int first[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    first[i] = run;
+    run += padded[i];
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid * PER + i;
+      if (e < E) {
+        counts[e] = tot[i];
+        offsets[e] = first[i];
+      }
+    }
+    if (tid == 255) offsets[E] = run;
+  }
+  // this group's tiles: first row = offsets[e] + earlier groups + earlier
+  // tiles of the group
+  const int t0 = g * kScanGroup;
+  const int nt = min(kScanGroup, ntiles - t0);
+  int c[kScanGroup][PER];
+#pragma unroll
+  for (int j = 0; j < kScanGroup; ++j)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid * PER + i;
+      c[j][i] = tile_base[(size_t)(t0 + min(j, nt - 1)) * E +
+                          (e < E ? e : E - 1)];
+    }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
+    int base = first[i] + pre[i];
+#pragma unroll
+    for (int j = 0; j < kScanGroup; ++j) {
+      if (j < nt && e < E) {
+        tile_base[(size_t)(t0 + j) * E + e] = base;
+        base += c[j][i];
       }
     }
   }
@@ -1243,8 +1379,22 @@ __global__ __launch_bounds__(512) void gate_reduce_small_kernel(
 
 // ------------------------------------------------------------------ launchers
 
-// What remains of moe_route after the gate kernels.
-enum { kRouteNeedPlan = 0, kRouteNeedScan = 1 };
+// What remains of moe_route after the gate kernels: the whole plan, the
+// one-workgroup scan (tile counts and ranks written by the gate's
+// epilogue), the tile histogram and the parallel scan, or the parallel scan
+// alone (histogram fused into the reduction).
+enum {
+  kRouteNeedPlan = 0,
+  kRouteNeedScan = 1,
+  kRouteNeedGroupHist = 2,
+  kRouteNeedGroupScan = 3
+};
+
+// Per-group expert totals of the parallel scan, after the partial logits.
+static int32_t* ws_groups(void* ws, int T, int E, int k) {
+  return (int32_t*)((unsigned char*)ws + ws_tile_bytes(T, E) +
+                    ws_rank_bytes(T, k) + ws_partial_bytes(T, E));
+}
 
 template <typename XT>
 static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
@@ -1322,13 +1472,20 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       const int KR = ((H + S - 1) / S + kq - 1) / kq * kq;
       S = (H + KR - 1) / KR;
       float* part = (float*)((unsigned char*)sr + ws_rank_bytes(T, k));
+      // group totals of the parallel scan, cleared by the partial gate
+      int32_t* gz = small ? nullptr
+                          : (int32_t*)((unsigned char*)part +
+                                       ws_partial_bytes(T, E));
+      const int gzn = small ? 0 : num_groups(T) * E;
       const dim3 pgrid(tiles, S, eg);
 #define MOE_GATE_PART(EPWV, TTV, DV)                                           \
   hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV>), pgrid,          \
-                     dim3(256), 0, s, x, w, T, H, E, KR, 64 * EPWV, part)
+                     dim3(256), 0, s, x, w, T, H, E, KR, 64 * EPWV, part, gz, \
+                     gzn)
 #define MOE_GATE_PART_X(EPWV, TTV, DV, DXV)                                    \
   hipLaunchKernelGGL((gate_partial_kernel<EPWV, TTV, 2, DV, DXV>), pgrid,     \
-                     dim3(256), 0, s, x, w, T, H, E, KR, 64 * EPWV, part)
+                     dim3(256), 0, s, x, w, T, H, E, KR, 64 * EPWV, part, gz, \
+                     gzn)
 #define MOE_GATE_PART_E(TTV)                                                   \
   do {                                                                         \
     if (epw == 1) MOE_GATE_PART(1, TTV, 4);                                    \
@@ -1340,7 +1497,8 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
       const int xg = (8 % S == 0 && tiles % (8 / S) == 0) ? 8 / S : 0;
 #define MOE_GATE_LDS_T(EPWV, TTV)                                              \
   hipLaunchKernelGGL((gate_partial_lds_kernel<EPWV, TTV>), dim3(tiles * S),   \
-                     dim3(512), 0, s, x, w, T, H, E, KR, tiles, xg, part)
+                     dim3(512), 0, s, x, w, T, H, E, KR, tiles, xg, part, gz, \
+                     gzn)
 #define MOE_GATE_LDS(EPWV)                                                     \
   do {                                                                         \
     if (TT == 8) MOE_GATE_LDS_T(EPWV, 4);                                      \
@@ -1348,16 +1506,17 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   } while (0)
       if (small) {
         hipLaunchKernelGGL((gate_partial_kernel<1, 2, 2, 2>), pgrid,
-                           dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw, part);
+                           dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw, part,
+                           gz, gzn);
       } else if (mid) {
         if (epg == 1)
           hipLaunchKernelGGL((gate_partial_kernel<1, 4, 2, 2>), pgrid,
                              dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw,
-                             part);
+                             part, gz, gzn);
         else
           hipLaunchKernelGGL((gate_partial_kernel<2, 4, 2, 2>), pgrid,
                              dim3(256), 0, s, x, w, T, H, E, KR, 64 * epw,
-                             part);
+                             part, gz, gzn);
       } else if (lds_gate) {
         if (epw == 1) MOE_GATE_LDS(1);
         else if (epw == 2) MOE_GATE_LDS(2);
@@ -1404,7 +1563,7 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
 #define MOE_GATE_RQ(EPWV, WV, CHV)                                             \
   hipLaunchKernelGGL((gate_reduce_quad_kernel<EPWV, WV, CHV>), rgrid,         \
                      dim3(64 * WV), 0, s, part, S, T, E, k, bias, idx, tw,    \
-                     dbg, tb, sr)
+                     dbg, tb, sr, fuse ? gz : nullptr)
 #define MOE_GATE_RQ_W(EPWV, CHV)                                               \
   do {                                                                         \
     if (fuse) MOE_GATE_RQ(EPWV, 16, CHV);                                      \
@@ -1429,7 +1588,7 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
 #undef MOE_GATE_RQ_E
 #undef MOE_GATE_RQ_W
 #undef MOE_GATE_RQ
-      *stage = fuse ? kRouteNeedScan : kRouteNeedPlan;
+      *stage = fuse ? kRouteNeedGroupScan : kRouteNeedGroupHist;
       return hipGetLastError();
     }
 #define MOE_GATE_V2(EPWV, PQV, DV)                                         \
@@ -1468,6 +1627,32 @@ static hipError_t launch_scan(int32_t* tile_base, int nt, int E, int pad,
   return hipGetLastError();
 }
 
+// The rest of the plan after the gate kernels, by what they left to do.
+static hipError_t finish_plan(int stage, const int32_t* topk_idx, int T,
+                              int k, int E, int pad, int32_t* counts,
+                              int32_t* offsets, void* workspace,
+                              hipStream_t s) {
+  int32_t* tile_base = (int32_t*)workspace;
+  int32_t* slot_rank =
+      (int32_t*)((unsigned char*)workspace + ws_tile_bytes(T, E));
+  const int nt = num_tiles(T);
+  if (stage == kRouteNeedPlan)
+    return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
+  if (stage == kRouteNeedScan)
+    return launch_scan(tile_base, nt, E, pad, counts, offsets, s);
+  int32_t* gtot = ws_groups(workspace, T, E, k);
+  if (stage == kRouteNeedGroupHist) {
+    hipLaunchKernelGGL(tile_histogram_kernel, dim3(nt), dim3(256), 0, s,
+                       topk_idx, T, k, E, tile_base, slot_rank, gtot);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(expert_scan_groups_kernel, dim3(num_groups(T)),
+                     dim3(256), 0, s, tile_base, nt, E, pad, gtot,
+                     num_groups(T), counts, offsets);
+  return hipGetLastError();
+}
+
 // The gate kernels of moe_route; *stage says what remains (plan or scan).
 static hipError_t launch_gate(const void* x, const void* w, int xdt,
                               const float* bias, int T, int H, int E, int k,
@@ -1498,10 +1683,8 @@ hipError_t launch_route(const void* x, const void* w, int xdt,
   hipError_t err = launch_gate(x, w, xdt, bias, T, H, E, k, topk_idx, topk_w,
                                logits_dbg, workspace, &stage, s);
   if (err != hipSuccess) return err;
-  if (stage == kRouteNeedPlan)
-    return launch_plan(topk_idx, T, k, E, pad, counts, offsets, workspace, s);
-  return launch_scan((int32_t*)workspace, num_tiles(T), E, pad, counts,
-                     offsets, s);
+  return finish_plan(stage, topk_idx, T, k, E, pad, counts, offsets,
+                     workspace, s);
 }
 
 // moe_route then moe_dispatch.  When the top-k leaves the plan to do for at
@@ -1527,8 +1710,8 @@ hipError_t launch_route_dispatch(const void* x, const void* w, int xdt,
       return launch_plan_dispatch_small(x, xdt, T, H, topk_idx, k, E, pad,
                                         counts, offsets, pdt, rows, capacity,
                                         row_scales, row_src, tok_row, s);
-    err = launch_scan((int32_t*)workspace, num_tiles(T), E, pad, counts,
-                      offsets, s);
+    err = finish_plan(stage, topk_idx, T, k, E, pad, counts, offsets,
+                      workspace, s);
   } else {
     err = launch_route(x, w, xdt, bias, T, H, E, k, pad, topk_idx, topk_w,
                        counts, offsets, logits_dbg, workspace, s);
@@ -1554,7 +1737,7 @@ hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,
   }
   if (nt > 0) {
     hipLaunchKernelGGL(tile_histogram_kernel, dim3(nt), dim3(256), 0, s,
-                       topk_idx, T, k, E, tile_base, slot_rank);
+                       topk_idx, T, k, E, tile_base, slot_rank, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
