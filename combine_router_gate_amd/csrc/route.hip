@@ -586,8 +586,17 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
       }
       lds_barrier();
       // no prefetch past the range: with few steps per range (few tokens,
-      // fine hidden split) those loads would double the traffic; steps past
-      // the range still run (zero x) on the registers' stale finite weights
+      // fine hidden split) those loads would double the traffic.  Steps past
+      // the range still run on zero x, and weight elements outside the range
+      // (stale registers, or the next range's columns) are zeroed too, so a
+      // non-finite weight there cannot turn 0 * w into NaN
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) {
+        const bool wok = k_lo + i * KS + g * (8 * PQ) + q * 8 < k_hi;
+#pragma unroll
+        for (int et = 0; et < EPW; ++et)
+          if (!wok) wreg[j][et][q] = z;
+      }
       if (i + DX < nss) load_x(i + DX, xreg[jx]);
 #pragma unroll
       for (int q = 0; q < PQ; ++q) {

@@ -173,3 +173,29 @@ def test_errors_raise():
         moe.moe_combine_residual(y, d["tok_row"], p["topk_w"], None, res, res,
                                  res, None)           # rnr aliases residual
     torch.cuda.synchronize()
+
+
+def test_route_nonfinite_weight_stays_in_its_logit():
+    """An infinite gate weight inside one hidden range: that expert's logit
+    is +inf (the fp64 oracle's value) and every other logit stays finite and
+    within tolerance.  H = 192 over three 64-wide ranges makes each range one
+    step, so the split gate runs a step past every range; weights outside a
+    range must not meet that step's zero x as 0 * inf = NaN."""
+    cfg = I.CONFIGS["dsv3_decode"].with_shape(T=64, H=192, E=64, k=4, pad=8)
+    note("route with an infinite gate weight, T=64 H=192 E=64")
+    wl = I.make_workload(cfg, 2)
+    x = wl.x.values.copy()
+    x[:, 100] = 1.0
+    w = wl.w_gate.values.copy()
+    w[5, 100] = np.inf
+    xb = I._pack(x, "bf16")
+    wb = I._pack(w, "bf16")
+    p = moe.route(to_dev(xb), to_dev(wb), cfg.k, cfg.pad, want_logits=True)
+    torch.cuda.synchronize()
+    gl = to_host(p["logits"]).astype(np.float64)
+    o = O.gate_logits(xb.values, wb.values)
+    assert np.isposinf(o[:, 5]).all()
+    assert np.isposinf(gl[:, 5]).all(), gl[:, 5][:8]
+    rest = np.delete(np.arange(cfg.E), 5)
+    assert np.isfinite(gl[:, rest]).all()
+    assert np.abs(gl[:, rest] - o[:, rest]).max() <= 1e-4
