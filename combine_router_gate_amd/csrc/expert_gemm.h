@@ -8,13 +8,13 @@
 
 namespace moe {
 
-constexpr int kGemmRowsPerTile = 128;   // output rows per workgroup tile
+constexpr int kGemmRowsPerTile = 256;   // output rows per workgroup tile
 constexpr int kGemmMaxK = 8192;
 
-// Upper bound on the 128-row tiles of all expert segments (also bounds the
-// number of tiles of any larger row count).
+// Upper bound on the row tiles of all expert segments: each segment has at
+// most one partial tile.
 inline long long gemm_row_tiles(size_t rows_capacity, int E) {
-  return (long long)((rows_capacity + 127) / 128) + E;
+  return (long long)((rows_capacity + kGemmRowsPerTile - 1) / kGemmRowsPerTile) + E;
 }
 inline size_t gemm_workspace_bytes(size_t rows_capacity, int E) {
   return ((size_t)gemm_row_tiles(rows_capacity, E) * 8 + 255) & ~size_t(255);

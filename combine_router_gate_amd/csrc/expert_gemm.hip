@@ -93,50 +93,112 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
         tiles[start[e] + j] = make_int2(e, off[e] + j * tm);
 }
 
-// A workgroup computes a TMR (rows, 128 or 256) x 256 (columns) tile with 8
-// waves (two per SIMD); wave (wm, wn) owns rows TMR/2 wm .. +TMR/2 and
-// columns 64 wn .. +64, i.e. TMR/32 x 4 MFMA tiles.  Per 128-wide block each
-// wave loads TMR/128 row groups of the activation tile and two of the
-// weight tile (16 rows x 128 bytes each) into registers two blocks ahead and
-// writes them to LDS one block ahead (two LDS stages), swizzled so that
-// every ds_write_b128 and ds_read_b128 is conflict-free.  The activation
-// scales of the tile's rows, all blocks, are copied to LDS once at the start
-// (one scattered 4-byte load per row and block measured slower).  Per
-// activation fragment, 4 MFMAs are issued back to back into separate result
-// registers and then scaled into the fp32 accumulators, so one wave's
-// scaling runs while the other wave's MFMAs occupy the matrix core.  A tile
-// whose second row half lies past its segment skips that half's copies and
-// MFMAs.
-constexpr int kTN = 256;
-template <int TMR> struct GemmTile {
-  static constexpr int A = TMR * 128, B = kTN * 128;
-  static constexpr int Stage = A + B;
-  static constexpr int MI = TMR / 32;               // row fragments per wave
-  static constexpr int AG = TMR / 128;              // row groups copied per wave
-};
+// A workgroup computes a 256 (rows) x 256 (columns) tile with 8 waves (two
+// per SIMD); wave (wm, wn) owns rows 128 wm .. +128 and columns 64 wn .. +64,
+// i.e. 8 x 4 MFMA tiles: 12 fragments read from LDS per 32 MFMAs.  Operands
+// reach LDS through direct global->LDS copies, two stages: while block b is
+// computed from one stage, block b + 1 is copied into the other, and one
+// wait plus barrier per block hands the stages over.  Each wave copies 32
+// activation rows and 32 weight rows (16 rows x 128 bytes per group) and the
+// activation scales of its rows for that block.  Rows sit in LDS with an XOR
+// swizzle of their 16-byte pieces that keeps the fragment reads free of bank
+// conflicts.
+//
+// The block's work is software-pipelined per wave: the activation fragment
+// of step i + 1 is read while the 4 MFMAs of step i run, and the products of
+// step i are scaled into the fp32 accumulators during step i + 1 (those of
+// the block's last step during the next block's first), so neither the LDS
+// latency nor the MFMA latency sits between dependent instructions.  Right
+// after the barrier the next block's weight fragments and first activation
+// fragment are read while the last MFMAs drain.  A tile whose second row
+// half lies past its segment skips that half's fragment reads and MFMAs.
+constexpr int kTM = 256, kTN = 256;
+constexpr int kStageA = kTM * 128, kStageB = kTN * 128;
+constexpr int kStage = kStageA + kStageB;   // 64 KiB
+constexpr int kMI = 8;                      // row fragments per wave
 
-template <int YT, int TMR>
+// Direct global->LDS copy of 16 (or 4) bytes per lane from base + off: lane
+// l's data lands at lds + 16 l (+ 4 l).  Issued from inline assembly so the
+// compiler, which would otherwise wait for every copy in flight before any
+// LDS read, leaves the waiting to the pipeline below (s_waitcnt vmcnt(n)
+// counts these copies in issue order).  The copy takes its LDS address from
+// M0, which is saved and restored around it; one wait state separates the
+// write of M0 from the copy that reads it.  The copy has no register result.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void copy_to_lds16(const void* base, uint32_t off,
+                                              uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(uniform_ptr(base)),
+        "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+__device__ __forceinline__ void copy_to_lds4(const void* base, uint32_t off,
+                                             uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(uniform_ptr(base)),
+        "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Work order: the hardware places workgroup ids round-robin over the 8
+// XCDs (id % 8), each with its own L2.  Row tiles go in groups of G =
+// 8 / gcd(ntn, 8), so that a group holds a multiple of 8 workgroups, and
+// inside a group column tiles go in chunks of 8, each chunk holding its 8
+// columns for every row tile of the group.  Column tile nt then runs on XCD
+// nt % 8 for every row tile (the last ntn % 8 columns excepted), so all row
+// tiles of an expert find its weight panels in one L2, while a row tile's
+// activation panel is shared by the column tiles on every XCD.
+__device__ __forceinline__ int row_group(int ntn) {
+  const int g = ntn & 7;   // gcd(ntn, 8) is 8, 4, 2 or 1
+  return g == 0 ? 1 : (g & 3) == 0 ? 2 : (g & 1) == 0 ? 4 : 8;
+}
+__device__ __forceinline__ void tile_of(int bid, int ntn, int* mt, int* nt) {
+  const int G = row_group(ntn);
+  const int grp = bid / (G * ntn);
+  const int rem = bid - grp * G * ntn;
+  const int full = (ntn / 8) * 8 * G;
+  if (rem < full) {
+    const int chunk = rem / (8 * G), within = rem - chunk * 8 * G;
+    *mt = G * grp + within / 8;
+    *nt = 8 * chunk + (within & 7);
+  } else {
+    const int tail = ntn & 7;
+    *mt = G * grp + (rem - full) / tail;
+    *nt = (ntn / 8) * 8 + (rem - full) % tail;
+  }
+}
+
+template <int YT>
 __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     const unsigned char* __restrict__ rows, const float* __restrict__ rscale,
     int K, int cap, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ offsets, const unsigned char* __restrict__ w,
     const float* __restrict__ wscale, int N, unsigned char* __restrict__ y,
-    const int2* __restrict__ tiles, int mt_ub, int ntn, int gn) {
-  using G = GemmTile<TMR>;
-  // one LDS object per stage, so the compiler can tell the block being read
-  // from the block being written
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::Stage];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::Stage];
+    const int2* __restrict__ tiles, int mt_ub, int ntn) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kStage];
   __shared__ float sw[2][kGemmMaxK / 128];
-  // the tile's activation scales, all blocks (row stride padded by one float
-  // so the 16 rows of a fragment read distinct banks)
-  constexpr int kRS = kGemmMaxK / 128 + 1;
-  __shared__ float rsc[TMR * kRS];
-  const int bid = blockIdx.x;
-  const int ng = bid / (mt_ub * gn);
-  const int rem = bid - ng * mt_ub * gn;
-  const int mt = rem / gn;
-  const int nt = ng * gn + (rem - mt * gn);
+  // activation scales of the stage's block: wave v copies rows 32 v .. +31
+  // (lanes 32..63 repeat them) to rsr[stage][64 v .. 64 v + 63]
+  __shared__ __attribute__((aligned(256))) float rsr[2][8 * 64];
+  int mt, nt;
+  tile_of(blockIdx.x, ntn, &mt, &nt);
   if (mt >= mt_ub || nt >= ntn) return;
   const int2 tile = tiles[mt];
   const int e = tile.x;
@@ -144,7 +206,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   const int r0 = tile.y;
   int r_end = offsets[e + 1];
   r_end = r_end > cap ? cap : r_end;
-  r_end = r_end < r0 + TMR ? r_end : r0 + TMR;
+  r_end = r_end < r0 + kTM ? r_end : r0 + kTM;
   if (r_end <= r0) return;
   const int KB = K / 128;
   const int NB = N / 128;
@@ -153,159 +215,143 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
   const int c16 = lane & 15, g4 = lane >> 4;
   const int wm = wv & 1, wn = wv >> 1;
   // this wave's row half holds rows of the segment (uniform per wave)
-  const bool half_live = (TMR / 2) * wm < r_end - r0;
+  const bool half_live = 128 * wm < r_end - r0;
 
-  // weight scales of the tile's two 128-column blocks, and the activation
-  // scales of its rows (one coalesced copy of TMR * KB consecutive floats;
-  // rows past the segment repeat its last row and are never stored)
+  // weight scales of the tile's two 128-column blocks
   for (int i = tid; i < 2 * KB; i += 512) {
     const int h = i / KB, b = i - h * KB;
     const int nb = nt * 2 + h < NB ? nt * 2 + h : NB - 1;
     sw[h][b] = wscale[((size_t)e * NB + nb) * KB + b];
   }
-  for (int i = tid; i < TMR * KB; i += 512) {
-    const int rr = i / KB, b = i - rr * KB;
-    const int r = r0 + rr < r_end ? r0 + rr : r_end - 1;
-    rsc[rr * kRS + b] = rscale[(size_t)r * KB + b];
-  }
 
-  // Copies are coalesced: a 16-row x 128-byte group is two loads of 8 rows,
-  // 8 lanes per row reading its 128 bytes (piece p = lane & 7).  In LDS a
-  // group keeps its rows in order, 128 bytes each, with 16-byte piece p of
-  // row r at slot p ^ swz(r); the fragment of lane (g, c) is pieces 2g and
-  // 2g + 1 of row c.  This swizzle keeps both the 16-byte writes (8 lanes
-  // per row) and the fragment reads (16 lanes, 16 rows) free of LDS bank
-  // conflicts on gfx950 (a fragment-order layout measured 2-way conflicts on
-  // its writes, half of the kernel's LDS cycles).
-  auto row_ofs = [](int r, int p) {                  // byte offset in a group
-    return r * 128 + ((p ^ ((r & 7) ^ ((r >> 3) & 1))) * 16);
-  };
+  // A 16-row x 128-byte group is two copies of 8 rows, 8 lanes per row.  In
+  // LDS a group keeps its rows in order, 128 bytes each, with 16-byte piece
+  // p of row r at slot p ^ swz(r); a copy writes lane l at slot l & 7 of row
+  // l >> 3, so lane l reads piece (l & 7) ^ swz(row) of its row.  The
+  // fragment of lane (g, c) is pieces 2g and 2g + 1 of row c.  The swizzle
+  // keeps the fragment reads (16 lanes, 16 rows) free of bank conflicts.
+  auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+  auto row_ofs = [&](int r, int p) { return r * 128 + ((p ^ swz(r)) * 16); };
   const int lp = lane & 7, lr = lane >> 3;
-  int wofs[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) wofs[u] = row_ofs(8 * u + lr, lp);
   const int rofs0 = row_ofs(c16, 2 * g4), rofs1 = row_ofs(c16, 2 * g4 + 1);
-  // this lane's sources (block 0) as 32-bit byte offsets from uniform
-  // bases (cap * K and N * K fit in 32 bits); block b adds b * 128
+  // this lane's sources (block 0) as 32-bit byte offsets from uniform bases
+  // (cap * K and N * K fit in 32 bits); block b moves the bases by b * 128.
+  // Rows past the segment repeat its last row (copied, never stored).
   const unsigned char* wexp = w + (size_t)e * N * K;
-  uint32_t aoff[G::AG][2];
-  bool aload[G::AG];
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int q = 0; q < G::AG; ++q) {
-    const int grp = G::AG * wv + q;
-    aload[q] = 16 * grp < r_end - r0;          // row group holds segment rows
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      int r = r0 + 16 * grp + 8 * u + lr;
+      int r = r0 + 32 * wv + 16 * h + 8 * u + lr;
       r = r < r_end ? r : r_end - 1;
-      aoff[q][u] = (uint32_t)r * (uint32_t)K + 16 * lp;
-    }
-  }
-  uint32_t boff[2][2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int n = nt * kTN + 16 * (2 * wv + q) + 8 * u + lr;
+      aoff[2 * h + u] = (uint32_t)r * (uint32_t)K + 16 * (lp ^ swz(8 * u + lr));
+      int n = nt * kTN + 32 * wv + 16 * h + 8 * u + lr;
       n = n < N ? n : N - 1;
-      boff[q][u] = (uint32_t)n * (uint32_t)K + 16 * lp;
+      boff[2 * h + u] = (uint32_t)n * (uint32_t)K + 16 * (lp ^ swz(8 * u + lr));
     }
+  int sr = r0 + 32 * wv + (lane & 31);
+  sr = sr < r_end ? sr : r_end - 1;
+  const uint32_t soff = (uint32_t)sr * (uint32_t)KB * 4u;
 
-  f32x4 acc[G::MI][4];
+  // the 9 copies of block b into one stage (same count for every wave)
+  auto copy_block = [&](int b, unsigned char* stage, float* scales) {
+    const uint32_t o = (uint32_t)b * 128u;
 #pragma unroll
-  for (int i = 0; i < G::MI; ++i)
+    for (int q = 0; q < 4; ++q)
+      copy_to_lds16(rows + o, aoff[q],
+                    lds_addr(stage + (2 * wv + (q >> 1)) * 2048 + (q & 1) * 1024));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      copy_to_lds16(wexp + o, boff[q],
+                    lds_addr(stage + kStageA + (2 * wv + (q >> 1)) * 2048 +
+                             (q & 1) * 1024));
+    copy_to_lds4(rscale + b, soff, lds_addr(scales + 64 * wv));
+  };
+
+  f32x4 acc[kMI][4];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // staging through registers: block b + 1 is loaded during block b - 1 and
-  // written to LDS at the start of block b
-  u32x4 ra_[G::AG][2], rb_[2][2];
-  auto load_regs = [&](int b) {
-    const size_t o = (size_t)b * 128;
-#pragma unroll
-    for (int q = 0; q < G::AG; ++q)
-      if (aload[q]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) ra_[q][u] = ld16(rows + aoff[q][u] + o);
-      }
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) rb_[q][u] = ld16(wexp + boff[q][u] + o);
+  auto read_frag = [&](const unsigned char* p) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p + rofs0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + rofs1);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  auto store_regs = [&](unsigned char* base) {
-#pragma unroll
-    for (int q = 0; q < G::AG; ++q)
-      if (aload[q]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          *reinterpret_cast<u32x4*>(base + (G::AG * wv + q) * 2048 + wofs[u]) =
-              ra_[q][u];
-      }
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<u32x4*>(base + G::A + (2 * wv + q) * 2048 +
-                                  wofs[u]) = rb_[q][u];
+  // scale of row 128 wm + 16 i + c16, copied by wave 4 wm + i / 2
+  auto row_scale = [&](const float* scales, int i) {
+    return scales[(4 * wm + i / 2) * 64 + 16 * (i & 1) + c16];
   };
-
-  auto block = [&](int b, const unsigned char* base, unsigned char* next1) {
-    __builtin_amdgcn_sched_barrier(0);   // keep blocks apart
-    // unconditional (clamped) copies keep the compiler's wait counts
-    // exact; past the last block they are redundant and never read
-    lds_barrier();
-    store_regs(next1);
-    load_regs(b + 2 < KB ? b + 2 : KB - 1);
-    if (!half_live) return;
-    const float* sa = rsc + ((TMR / 2) * wm) * kRS + b;
+  i32x8 fb[4], fa;
+  f32x4 pp[4];        // products of the previous step, not yet scaled
+  float sp = 0.f;     // their scale
+  auto load_block = [&](const unsigned char* base) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = read_frag(base + kStageA + (4 * wn + j) * 2048);
+    fa = read_frag(base + (kMI * wm) * 2048);
+  };
+  auto retire = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pp[j][q], sp, acc[i][j][q]);
+  };
+  // block b from stage `base`; fb and fa of step 0 are already loaded
+  auto compute = [&](int b, const unsigned char* base, const float* scales) {
     const float swb = sw[wn >> 1][b];
-    i32x8 fb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned char* pb = base + G::A + (4 * wn + j) * 2048;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + rofs0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + rofs1);
-      fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int i = 0; i < G::MI; ++i) {
-      const unsigned char* pa = base + (G::MI * wm + i) * 2048;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + rofs0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + rofs1);
-      const i32x8 fa = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const float si = sa[(16 * i + c16) * kRS] * swb;
+    for (int i = 0; i < kMI; ++i) {
+      i32x8 fn;
+      if (i + 1 < kMI) fn = read_frag(base + (kMI * wm + i + 1) * 2048);
+      const float si = row_scale(scales, i) * swb;
       f32x4 p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      if (i > 0) retire(i - 1);
+      else if (b > 0) retire(kMI - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[j][q], si, acc[i][j][q]);
+      for (int j = 0; j < 4; ++j) pp[j] = p[j];
+      sp = si;
+      if (i + 1 < kMI) fa = fn;
     }
   };
-  load_regs(0);
-  store_regs(lds0);
-  load_regs(KB > 1 ? 1 : 0);
-  __syncthreads();   // sw (and block 0) visible
-  // block b reads stage b % 2; two blocks per iteration with no branch
-  // between them (exact wait counts), then the last one
+  // block b: copy block b + 1 into the stage block b - 1 used, compute block
+  // b, wait for this wave's copies and meet the other waves (stage b + 1 is
+  // complete and nobody reads stage b any more), then read block b + 1's
+  // first fragments
+  auto step = [&](int b, const unsigned char* cur, const float* cur_s,
+                  unsigned char* nxt, float* nxt_s) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + 1 < KB) copy_block(b + 1, nxt, nxt_s);
+    if (half_live) compute(b, cur, cur_s);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                 ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (half_live && b + 1 < KB) load_block(nxt);
+  };
+  __syncthreads();   // sw visible; no load of this wave in flight
+  copy_block(0, lds0, rsr[0]);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+               ::: "memory");
+  if (half_live) load_block(lds0);
   int b = 0;
   for (; b + 2 <= KB; b += 2) {
-    block(b, lds0, lds1);
-    block(b + 1, lds1, lds0);
+    step(b, lds0, rsr[0], lds1, rsr[1]);
+    step(b + 1, lds1, rsr[1], lds0, rsr[0]);
   }
-  if (b < KB) block(b, lds0, lds1);
+  if (b < KB) step(b, lds0, rsr[0], lds1, rsr[1]);
+  if (!half_live) return;   // no copy in flight: every step waited for them
+  retire(kMI - 1);
 
-  // lane: row TMR/2 wm + 16 i + c16, columns 64 wn + 16 j + 4 g4 .. + 3
-  if (!half_live) return;
+  // lane: row 128 wm + 16 i + c16, columns 64 wn + 16 j + 4 g4 .. + 3
 #pragma unroll
-  for (int i = 0; i < G::MI; ++i) {
-    const int r = r0 + (TMR / 2) * wm + 16 * i + c16;
+  for (int i = 0; i < kMI; ++i) {
+    const int r = r0 + 128 * wm + 16 * i + c16;
     if (r >= r_end) continue;
     const bool live = row_src == nullptr || row_src[r] >= 0;
 #pragma unroll
@@ -330,32 +376,28 @@ hipError_t launch_expert_gemm(const void* rows, const float* row_scales,
                               int E, const void* w, const float* w_scales,
                               int N, void* y, int y_dtype, void* workspace,
                               hipStream_t s) {
-  constexpr int TMR = kGemmRowsPerTile;
   const long long mt_ub = gemm_row_tiles(rows_capacity, E);
   int2* tiles = (int2*)workspace;
   const int cap = (int)rows_capacity;
   hipLaunchKernelGGL(gemm_tile_map_kernel, dim3(1), dim3(512), 0, s, offsets,
-                     E, cap, (int)mt_ub, TMR, tiles);
+                     E, cap, (int)mt_ub, kTM, tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // all column tiles of a row tile are consecutive: the row tile's
-  // activations stay in cache while the expert's weight panels stream
   const int ntn = (N + kTN - 1) / kTN;
-  const int gn = ntn;
-  const long long grid = mt_ub * gn;
+  // row tiles in groups of G (tile_of), every column tile of each
+  const int G = (ntn & 7) == 0 ? 1 : (ntn & 3) == 0 ? 2 : (ntn & 1) == 0 ? 4 : 8;
+  const long long grid = (mt_ub + G - 1) / G * G * ntn;
   const unsigned char* rb = (const unsigned char*)rows;
   const unsigned char* wb = (const unsigned char*)w;
   unsigned char* yb = (unsigned char*)y;
   if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<1, TMR>), dim3((unsigned)grid),
+    hipLaunchKernelGGL(expert_gemm_fp8_kernel<1>, dim3((unsigned)grid),
                        dim3(512), 0, s, rb, row_scales, K, cap, row_src,
-                       offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
-                       gn);
+                       offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn);
   else
-    hipLaunchKernelGGL((expert_gemm_fp8_kernel<0, TMR>), dim3((unsigned)grid),
+    hipLaunchKernelGGL(expert_gemm_fp8_kernel<0>, dim3((unsigned)grid),
                        dim3(512), 0, s, rb, row_scales, K, cap, row_src,
-                       offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn,
-                       gn);
+                       offsets, wb, w_scales, N, yb, tiles, (int)mt_ub, ntn);
   return hipGetLastError();
 }
 
