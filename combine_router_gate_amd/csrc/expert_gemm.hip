@@ -117,45 +117,6 @@ constexpr int kStageA = kTM * 128, kStageB = kTN * 128;
 constexpr int kStage = kStageA + kStageB;   // 64 KiB
 constexpr int kMI = 8;                      // row fragments per wave
 
-// Direct global->LDS copy of 16 (or 4) bytes per lane from base + off: lane
-// l's data lands at lds + 16 l (+ 4 l).  Issued from inline assembly so the
-// compiler, which would otherwise wait for every copy in flight before any
-// LDS read, leaves the waiting to the pipeline below (s_waitcnt vmcnt(n)
-// counts these copies in issue order).  The copy takes its LDS address from
-// M0, which is saved and restored around it; one wait state separates the
-// write of M0 from the copy that reads it.  The copy has no register result.
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ void copy_to_lds16(const void* base, uint32_t off,
-                                              uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(uniform_ptr(base)),
-        "s"(__builtin_amdgcn_readfirstlane(lds))
-      : "memory");
-}
-__device__ __forceinline__ void copy_to_lds4(const void* base, uint32_t off,
-                                             uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(uniform_ptr(base)),
-        "s"(__builtin_amdgcn_readfirstlane(lds))
-      : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)p;
-}
-
 // Work order: the hardware places workgroup ids round-robin over the 8
 // XCDs (id % 8), each with its own L2.  Row tiles go in groups of G =
 // 8 / gcd(ntn, 8), so that a group holds a multiple of 8 workgroups, and
@@ -329,15 +290,13 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
     __builtin_amdgcn_sched_barrier(0);
     if (b + 1 < KB) copy_block(b + 1, nxt, nxt_s);
     if (half_live) compute(b, cur, cur_s);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
-                 ::: "memory");
+    copies_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (half_live && b + 1 < KB) load_block(nxt);
   };
   __syncthreads();   // sw visible; no load of this wave in flight
   copy_block(0, lds0, rsr[0]);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
-               ::: "memory");
+  copies_barrier();
   if (half_live) load_block(lds0);
   int b = 0;
   for (; b + 2 <= KB; b += 2) {

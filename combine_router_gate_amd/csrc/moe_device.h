@@ -109,6 +109,54 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ------------------------------------------------------------------ LDS copies
+
+// Direct global->LDS copy of 16 (or 4) bytes per lane from base + off: lane
+// l's data lands at lds + 16 l (+ 4 l).  Issued from inline assembly so the
+// compiler, which would otherwise wait for every copy in flight before any
+// LDS read, leaves the waiting to the caller's pipeline (s_waitcnt vmcnt(n)
+// counts these copies in issue order).  The copy takes its LDS address from
+// M0, which is saved and restored around it; one wait state separates the
+// write of M0 from the copy that reads it.  The copy has no register result.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void copy_to_lds16(const void* base, uint32_t off,
+                                              uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(uniform_ptr(base)),
+        "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+__device__ __forceinline__ void copy_to_lds4(const void* base, uint32_t off,
+                                             uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(uniform_ptr(base)),
+        "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Wait for this wave's copies and LDS operations, then meet the other waves:
+// every copy the workgroup issued before the barrier has landed.
+__device__ __forceinline__ void copies_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+               ::: "memory");
+}
+
 // ------------------------------------------------------------------ keys
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).

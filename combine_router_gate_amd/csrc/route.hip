@@ -22,7 +22,11 @@
 //    of 64 experts per workgroup) writes the partial logits, and
 //    gate_reduce_quad_kernel (gate_reduce_small_kernel up to 512 tokens)
 //    sums them in range order and selects the top-k.  Where a split
-//    would not pay, gate_topk_v2_kernel does all of it in one pass.  x is
+//    would not pay, gate_topk_v2_kernel does all of it in one pass.  A
+//    narrow gate (weight under 1 MiB, 4096 to 32768 tokens) skips the
+//    split: gate_topk_narrow_kernel runs 32 tokens x all experts per
+//    workgroup, each streaming the whole weight from L2 through LDS, with
+//    the top-k in its epilogue.  x is
 //    read with ordinary (allocating) loads, so the dispatch that reads it
 //    next finds much of it still in the memory-attached cache.
 //  * E < 64 (memory-bound gate): the 4 waves split the hidden dimension of a
@@ -482,6 +486,131 @@ __global__ __launch_bounds__(256, 1) void gate_topk_v2_kernel(
     const int e = tile_sel[tl * MOE_MAX_TOPK + j];
     slot_rank[(size_t)t0 * k + q] = __popcll(tile_bits[e] & ((1ull << tl) - 1ull));
   }
+}
+
+// One pass of gate and top-k for a narrow gate (E * H small enough that
+// every workgroup can stream the whole gate weight from L2): 32 tokens x
+// all experts per workgroup of 8 waves, so there are twice as many
+// workgroups as 64-token tiles and no partial logits go through HBM.  Per
+// 64-wide k step both operands reach LDS through direct global->LDS copies
+// (8 lanes per 128-byte row segment, 8 rows per copy; a lane fetches source
+// piece (l & 7) ^ gate_lds_swz(row), so the row swizzle of the other gate
+// kernels holds) into two stages: step i + 1 is copied while step i is
+// computed, then one wait plus barrier hands the stages over (per wave 2 EPW
+// weight groups, plus one x group on waves 0..3).  Wave wv owns expert
+// tiles EPW wv .. +EPW (16 experts each) for both 16-token halves.  The
+// logits then go through LDS so each 16-lane group holds one token's
+// experts for the top-k (one token per group, one pass).  The kernel clears
+// the per-group totals that the tile histogram of the same call
+// accumulates.  Requires H % 64 == 0 and byte offsets of x and w below 2^32.
+template <int EPW>
+__global__ __launch_bounds__(512, 1) void gate_topk_narrow_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int T, int H, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits_dbg, int32_t* __restrict__ gzero,
+    int gzero_n) {
+  clear_group_totals(gzero, gzero_n);
+  constexpr int TOK = 32;
+  constexpr int ET = 8 * EPW;              // expert tiles of the workgroup
+  constexpr int EP = 16 * ET;              // padded experts
+  constexpr int LROW = EP + 4;             // logits row stride (floats)
+  constexpr int XS = TOK * 128;            // bytes of x in one stage
+  constexpr int STG = XS + EP * 128;       // bytes of one stage
+  constexpr int WPW = 2 * EPW;             // weight copies per wave and step
+  constexpr int LDS_BYTES = (TOK * LROW * 4 > 2 * STG) ? TOK * LROW * 4 : 2 * STG;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * TOK;
+  const int nss = H / 64;
+  const int lr = lane >> 3;
+  const bool xwave = wv < 4;               // copies x rows 8 wv .. +7
+
+  // byte offsets of this lane's source pieces (step 0); lane l copies piece
+  // slot l & 7 of row l >> 3 of its 8-row group
+  uint32_t xoff, woff[WPW];
+  {
+    const int r = 8 * (wv & 3) + lr;
+    const uint32_t row = (uint32_t)min(t0 + r, T - 1);
+    xoff = row * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ gate_lds_swz(r)) * 16);
+  }
+#pragma unroll
+  for (int m = 0; m < WPW; ++m) {
+    const int r = 8 * (wv + 8 * m) + lr;
+    const uint32_t row = (uint32_t)min(r, E - 1);
+    woff[m] = row * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ gate_lds_swz(r)) * 16);
+  }
+  auto copy_step = [&](int i, unsigned char* stage) {
+    const unsigned char* xb = reinterpret_cast<const unsigned char*>(x) + (size_t)i * 128;
+    const unsigned char* wb = reinterpret_cast<const unsigned char*>(w) + (size_t)i * 128;
+    if (xwave) copy_to_lds16(xb, xoff, lds_addr(stage + wv * 1024));
+#pragma unroll
+    for (int m = 0; m < WPW; ++m)
+      copy_to_lds16(wb, woff[m], lds_addr(stage + XS + (wv + 8 * m) * 1024));
+  };
+
+  f32x4 acc[2][EPW];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragments: row r of the stage, piece 2 g + q
+  auto frag = [&](const unsigned char* stage, int r, int q) {
+    Frag<uint16_t> f;
+    f.v = *reinterpret_cast<const u32x4*>(stage + r * 128 + (((2 * g + q) ^ gate_lds_swz(r)) * 16));
+    return f;
+  };
+  auto compute = [&](const unsigned char* stage) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      Frag<uint16_t> a[2], b[EPW];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) a[tt] = frag(stage, tt * 16 + c16, q);
+#pragma unroll
+      for (int et = 0; et < EPW; ++et)
+        b[et] = frag(stage, TOK + (wv * EPW + et) * 16 + c16, q);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int et = 0; et < EPW; ++et) acc[tt][et] = mfma_step(a[tt], b[et], acc[tt][et]);
+    }
+  };
+
+  copy_step(0, lds);
+  copies_barrier();
+  for (int i = 0; i < nss; ++i) {
+    if (i + 1 < nss) copy_step(i + 1, lds + ((i + 1) & 1) * STG);
+    compute(lds + (i & 1) * STG);
+    copies_barrier();
+  }
+
+  // logits -> LDS [32 tokens][LROW] (bias added), then top-k per token
+  float* lg = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPW; ++et) {
+      const int e = (wv * EPW + et) * 16 + c16;
+      const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[(tt * 16 + g * 4 + i) * LROW + e] = acc[tt][et][i] + b;
+    }
+  __syncthreads();
+  const int tl = wv * 4 + g;
+  const int t = t0 + tl;
+  float v[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et) {
+    const int e = et * 16 + c16;
+    v[et] = lg[tl * LROW + e];
+    if (logits_dbg != nullptr && t < T && e < E)
+      logits_dbg[(size_t)t * E + e] = v[et];
+  }
+  topk_select_write<ET>(v, t, T, E, k, topk_idx, topk_w);
 }
 
 // ------------------------------------------------------------------ gate, split over H
@@ -1428,6 +1557,32 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   }
   const dim3 grid((T + 63) / 64);
   if constexpr (sizeof(XT) == 2) {
+    // Narrow gate (the whole weight under 1 MiB, e.g. H = 768 with 384
+    // experts): 32-token one-pass workgroups that each stream the whole
+    // weight from L2 beat the split gate, whose partial logits cost more
+    // than the GEMM itself; then the tile histogram and the parallel scan.
+    // Measured faster from 4096 to 32768 tokens with 64 to 512 experts
+    // (route at 8192 x 768 x 384: 40.5 -> 29 us); at 65536 tokens, with a
+    // 1 MiB weight, or with fewer experts (padded to 128 here) the split gate
+    // stays ahead.
+    const int en = (E + 127) / 128;
+    if (T >= 4096 && T <= 32768 && E >= 64 && E <= 512 && H % 64 == 0 &&
+        (size_t)E * H * 2 < ((size_t)1 << 20)) {
+      int32_t* gz = (int32_t*)((unsigned char*)sr + ws_rank_bytes(T, k) +
+                               ws_partial_bytes(T, E));
+      const int gzn = num_groups(T) * E;
+      const dim3 ngrid((T + 31) / 32);
+#define MOE_GATE_NARROW(EPWV)                                               \
+  hipLaunchKernelGGL((gate_topk_narrow_kernel<EPWV>), ngrid, dim3(512), 0, \
+                     s, x, w, bias, T, H, E, k, idx, tw, dbg, gz, gzn)
+      if (en == 1) MOE_GATE_NARROW(1);
+      else if (en == 2) MOE_GATE_NARROW(2);
+      else if (en == 3) MOE_GATE_NARROW(3);
+      else MOE_GATE_NARROW(4);
+#undef MOE_GATE_NARROW
+      *stage = kRouteNeedGroupHist;
+      return hipGetLastError();
+    }
     const int epw = gate_epw(E);
     // Split the hidden dimension so the partial GEMM runs about 256
     // workgroups; with a full chip that beats the fused single pass even

@@ -52,16 +52,17 @@ SMALL = {
     "small_t512": C["dsv3_decode"].with_shape(T=512, H=1024, k=6, pad=16),
     "small_t1": C["dsv3_decode"].with_shape(T=1, H=2048),
     # many tokens: the LDS-staged partial gate (2 and 1 expert tiles per
-    # wave, ragged token tile, 128-wide hidden ranges) and its fallback for
-    # H not a multiple of 128
-    "lds_gate_t4100_e100": C["dsv3_prefill"].with_shape(T=4100, H=512, E=100,
+    # wave, ragged token tile, 128-wide hidden ranges; gate weights of 1 MiB
+    # and more, below which the narrow one-pass gate runs) and its fallback
+    # for H not a multiple of 128
+    "lds_gate_t4100_e100": C["dsv3_prefill"].with_shape(T=4100, H=5248, E=100,
                                                         k=6, pad=32),
-    "lds_gate_t4096_e64": C["mixtral"].with_shape(T=4096, H=384, E=64, k=4,
+    "lds_gate_t4096_e64": C["mixtral"].with_shape(T=4096, H=8192, E=64, k=4,
                                                   pad=16),
     "gate_t4096_h1032": C["dsv3_decode"].with_shape(T=4096, H=1032, E=256),
     # 34 tiles of 128 tokens (the last ragged), S = 4: workgroups mapped so
     # each XCD serves one hidden range
-    "lds_gate_t4300_xcd": C["dsv3_prefill"].with_shape(T=4300, H=1024),
+    "lds_gate_t4300_xcd": C["dsv3_prefill"].with_shape(T=4300, H=2048),
     # few experts (E <= 32) and many bf16 tokens take the LDS-staged gate too
     "lds_gate_t4200_e24": C["mixtral"].with_shape(T=4200, H=512, E=24, k=3,
                                                   pad=16),
@@ -80,22 +81,34 @@ SMALL = {
                                               pad=16),
     # the most experts (512) with many tokens: split gate with 64-token
     # tiles, reduction in chunks of two ranges
-    "e512_t4096": C["moonep_skew"].with_shape(T=4096, H=256, E=512, k=8,
+    "e512_t4096": C["moonep_skew"].with_shape(T=4096, H=1024, E=512, k=8,
                                               zipf_bias=False),
+    # narrow one-pass gate (weight under 1 MiB, 4096..32768 tokens): 1, 2
+    # and 4 expert tiles per wave (3 is the MoonEP workload), padded
+    # experts, ragged last 32-token workgroup, a single 64-wide k step
+    "narrow_t4097_e100": C["dsv3_prefill"].with_shape(T=4097, H=512, E=100,
+                                                      k=6, pad=32),
+    "narrow_t6000_e200_h640": C["moonep_skew"].with_shape(T=6000, H=640,
+                                                          E=200),
+    "narrow_t5000_e512": C["moonep_skew"].with_shape(T=5000, H=256, E=512,
+                                                     zipf_bias=False),
+    "narrow_t4100_h64": C["dsv3_decode"].with_shape(T=4100, H=64, E=256),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 # gate shapes above 8192 tokens (route only: the dispatch and combine of
 # these sizes are the full workloads' paths): 128-token tiles with 3 hidden
 # ranges, and more than 16384 tokens (split gate, fused-histogram reduction)
 ROUTE_ONLY = {
-    "lds_gate_t10000_s3": C["dsv3_prefill"].with_shape(T=10000, H=1024),
-    "lds_gate_t20000": C["dsv3_prefill"].with_shape(T=20000, H=512),
+    "lds_gate_t10000_s3": C["dsv3_prefill"].with_shape(T=10000, H=2048),
+    "lds_gate_t20000": C["dsv3_prefill"].with_shape(T=20000, H=2048),
     # first shapes past each policy boundary: 513 tokens (64-token tiles
     # with expert groups), 8193 (128-token tiles), 16321 (64-token
     # reduction workgroups that build the tile histogram)
     "mid_t513": C["dsv3_decode"].with_shape(T=513, H=512),
-    "lds_gate_t8193": C["dsv3_prefill"].with_shape(T=8193, H=512),
-    "fused_hist_t16321": C["moonep_skew"].with_shape(T=16321, H=256),
+    "lds_gate_t8193": C["dsv3_prefill"].with_shape(T=8193, H=2048),
+    "fused_hist_t16321": C["moonep_skew"].with_shape(T=16321, H=1408),
+    # the narrow gate near its upper token bound
+    "narrow_t32768": C["moonep_skew"].with_shape(T=32768, H=256),
 }
 
 
@@ -187,12 +200,15 @@ INT_CASES = {
 # tokens than the partial-logit workspace holds).
 INT_LARGE = {
     "int_dsv3_prefill": C["dsv3_prefill"],
-    "int_fused_t16321_e384": C["moonep_skew"].with_shape(T=16321, H=256,
+    # split gate + fused-histogram reduction (weights of 1 MiB and more)
+    "int_fused_t16321_e384": C["moonep_skew"].with_shape(T=16321, H=1408,
                                                         zipf_bias=False),
-    "int_t20000": C["dsv3_prefill"].with_shape(T=20000, H=512),
+    "int_t20000": C["dsv3_prefill"].with_shape(T=20000, H=2048),
     "int_onepass_t300_e512_k16": C["moonep_skew"].with_shape(
         T=300, H=64, E=512, k=16, pad=8, zipf_bias=False),
-    "int_onepass_t5000_h64": C["dsv3_decode"].with_shape(T=5000, H=64),
+    # narrow one-pass gate, then tile histogram and parallel scan
+    "int_narrow_t5000_h64": C["dsv3_decode"].with_shape(T=5000, H=64),
+    "int_narrow_moonep": C["moonep_skew"].with_shape(zipf_bias=False),
     "int_onepass_t70000": C["mixtral"].with_shape(T=70000, H=128, E=64, k=4,
                                                   pad=16),
 }
