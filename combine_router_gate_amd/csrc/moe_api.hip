@@ -71,6 +71,15 @@ int check_route_shape(int T, int E, int k, int pad) {
   return MOE_OK;
 }
 
+// A gate over more than moe::kGateWideE experts takes bf16 x and at most
+// moe::kSplitMaxT tokens.
+int check_gate_wide(int T, int E, int x_dtype) {
+  if (E <= moe::kGateWideE) return MOE_OK;
+  if (x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T > moe::kSplitMaxT) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -115,6 +124,7 @@ int moe_route(const void* x, int x_dtype, int T, int H, const void* w_gate,
   if (st != MOE_OK) return st;
   if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if ((st = check_gate_wide(T, E, x_dtype)) != MOE_OK) return st;
   if (counts == nullptr || offsets == nullptr) return MOE_ERR_NULL;
   if (T > 0 && (x == nullptr || w_gate == nullptr || topk_idx == nullptr ||
                 topk_w == nullptr || workspace == nullptr))
@@ -248,6 +258,7 @@ int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
   if (st != MOE_OK) return st;
   if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if ((st = check_gate_wide(T, E, x_dtype)) != MOE_OK) return st;
   const bool fp8 = payload_dtype == MOE_FP8_E4M3;
   if (payload_dtype != x_dtype && !fp8) return MOE_ERR_DTYPE;
   if (fp8 && H % 128 != 0) return MOE_ERR_SHAPE;

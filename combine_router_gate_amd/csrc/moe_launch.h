@@ -30,8 +30,13 @@ constexpr int kSplitMax = 64;
 constexpr int kSplitMaxT = 65536;      // more tokens: the one-pass gate
 inline int gate_epw(int E) {           // expert tiles per wave of the gate
   const int et = (E + 15) / 16;
-  return et <= 4 ? 1 : et <= 8 ? 2 : et <= 16 ? 4 : et <= 24 ? 6 : 8;
+  return et <= 4 ? 1 : et <= 8 ? 2 : et <= 16 ? 4 : et <= 24 ? 6
+       : et <= 32 ? 8 : et <= 48 ? 12 : 16;
 }
+// Above this many experts the gate runs only the split bf16 path (partial
+// logits in expert groups, a 64-lane top-k per token), so x must be bf16
+// and T at most kSplitMaxT (where the workspace holds partial logits).
+constexpr int kGateWideE = 512;
 // Largest split of H for T tokens: 2 * kSplitRows partial rows, at least 4
 // ranges up to kSplitMaxT tokens.
 inline int split_max(int T) {

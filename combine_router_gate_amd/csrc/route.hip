@@ -1557,6 +1557,42 @@ static hipError_t launch_gate_typed(const XT* x, const XT* w, const float* bias,
   }
   const dim3 grid((T + 63) / 64);
   if constexpr (sizeof(XT) == 2) {
+    if (E > kGateWideE) {
+      // More than 512 experts (T <= kSplitMaxT, checked by the API):
+      // partial logits over hidden ranges in expert groups of 256 (also
+      // with a single range), then the top-k of each token over all 64
+      // lanes of a wave (16 logits per lane at 1024 experts) and the plan
+      // kernels.
+      const int epw = gate_epw(E);                 // 12 or 16
+      const int eg = epw / 4;
+      const int tiles = (T + 63) / 64;
+      int S = (256 + tiles * eg - 1) / (tiles * eg);
+      S = max(1, min(S, min(split_max(T), (H + 63) / 64)));
+      const int KR = ((H + S - 1) / S + 63) / 64 * 64;
+      S = (H + KR - 1) / KR;
+      float* part = (float*)((unsigned char*)sr + ws_rank_bytes(T, k));
+      hipLaunchKernelGGL((gate_partial_kernel<4, 4, 2, 4>),
+                         dim3(tiles, S, eg), dim3(256), 0, s, x, w, T, H, E,
+                         KR, 64 * epw, part, nullptr, 0);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      const int EPS = 64 * epw;
+      const bool few = T <= kSmallPlanT;   // one token per workgroup
+      const dim3 rgrid(few ? T : (T + 7) / 8);
+#define MOE_GATE_RS(C4V, TPWV)                                                \
+  hipLaunchKernelGGL((gate_reduce_small_kernel<C4V, TPWV>), rgrid, dim3(512), \
+                     0, s, part, S, EPS, T, E, k, bias, idx, tw, dbg)
+      if (epw == 12) {
+        if (few) MOE_GATE_RS(3, 1);
+        else MOE_GATE_RS(3, 8);
+      } else {
+        if (few) MOE_GATE_RS(4, 1);
+        else MOE_GATE_RS(4, 8);
+      }
+#undef MOE_GATE_RS
+      *stage = kRouteNeedPlan;
+      return hipGetLastError();
+    }
     // Narrow gate (the whole weight under 1 MiB, e.g. H = 768 with 384
     // experts): 32-token one-pass workgroups that each stream the whole
     // weight from L2 beat the split gate, whose partial logits cost more
@@ -1870,7 +1906,9 @@ hipError_t launch_route_dispatch(const void* x, const void* w, int xdt,
     err = launch_gate(x, w, xdt, bias, T, H, E, k, topk_idx, topk_w,
                       logits_dbg, workspace, &stage, s);
     if (err != hipSuccess) return err;
-    if (stage == kRouteNeedPlan)
+    // (its plan in LDS holds T / 64 x E bitmaps and first rows: up to 512
+    // experts)
+    if (stage == kRouteNeedPlan && E <= kGateWideE)
       return launch_plan_dispatch_small(x, xdt, T, H, topk_idx, k, E, pad,
                                         counts, offsets, pdt, rows, capacity,
                                         row_scales, row_src, tok_row, s);

@@ -92,7 +92,7 @@ const char* moe_status_string(int status);
 int moe_last_hip_error(void);
 
 /* Largest number of experts and of experts per token the kernels accept. */
-#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
 /*
@@ -144,7 +144,8 @@ size_t moe_workspace_bytes(int T, int E, int k);
  *   workspace  device scratch of workspace_bytes >= moe_workspace_bytes(T,E,k);
  *              read by the next moe_dispatch of the same tokens
  * Logits are accumulated in fp32 on the matrix cores (bf16 or fp32 inputs).
- * Limits: 1 <= E <= MOE_MAX_EXPERTS, H % 8 == 0, H >= 8.
+ * Limits: 1 <= E <= MOE_MAX_EXPERTS, H % 8 == 0, H >= 8; above 512 experts
+ * x must be bf16 (MOE_ERR_DTYPE) and T <= 65536 (MOE_ERR_SHAPE).
  */
 int moe_route(const void* x, int x_dtype, int T, int H,
               const void* w_gate, int E, const float* bias,
@@ -249,7 +250,8 @@ int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
  * between calls (each call rewrites what it reads).
  * Limit: moe_noalloc_scratch_bytes(T, E, k) <= MOE_NOALLOC_SCRATCH_BYTES
  * (8 MiB: about 4 bytes per slot plus 4 bytes per expert per 64 tokens;
- * 65536 tokens fit for every E <= 512 and k <= 16), else MOE_ERR_SCRATCH
+ * 65536 tokens fit for every E <= 512 with k <= 16 and E <= 1024 with
+ * k <= 8), else MOE_ERR_SCRATCH
  * before anything is enqueued.  Other errors as for moe_dispatch; MOE_ERR_HIP also
  * if the array's device address cannot be obtained.
  */

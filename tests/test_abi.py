@@ -61,7 +61,7 @@ def test_capacity_formula(L, T, E, k, pad):
 def test_capacity_invalid(L):
     assert moe.moe_rows_capacity(10, 4, 5, 1) == 0      # k > E
     assert moe.moe_rows_capacity(10, 0, 1, 1) == 0
-    assert moe.moe_rows_capacity(10, 513, 2, 1) == 0
+    assert moe.moe_rows_capacity(10, 1025, 2, 1) == 0
     assert moe.moe_rows_capacity(10, 8, 17, 1) == 0
     assert moe.moe_rows_capacity(10, 8, 2, 0) == 0
     assert moe.moe_rows_capacity(2 ** 30, 8, 8, 1) == 0  # rows overflow int32
@@ -101,7 +101,9 @@ def _route(L, **kw):
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(idx=None), NULL),
     (dict(counts=None), NULL), (dict(ws=None), NULL),
     (dict(k=17), SHAPE), (dict(k=0), SHAPE), (dict(E=0), SHAPE),
-    (dict(E=513), SHAPE), (dict(k=20, E=16), SHAPE), (dict(H=12), SHAPE),
+    (dict(E=1025), SHAPE), (dict(k=20, E=16), SHAPE), (dict(H=12), SHAPE),
+    # above 512 experts the gate takes bf16 x and at most 65536 tokens
+    (dict(E=600, xdt=0), DTYPE), (dict(E=600, T=65537), SHAPE),
     (dict(H=0), SHAPE), (dict(T=-1), SHAPE), (dict(pad=0), SHAPE),
     (dict(xdt=2), DTYPE), (dict(xdt=7), DTYPE),
     (dict(x=A[0] + 8), ALIGN), (dict(w=A[1] + 4), ALIGN),
@@ -159,7 +161,8 @@ def _route_dispatch(L, **kw):
     (dict(ws=None), NULL), (dict(row_src=None), NULL), (dict(pdt=2), NULL),
     (dict(scales=A[10]), DTYPE), (dict(xdt=2), DTYPE), (dict(pdt=0), DTYPE),
     (dict(pdt=2, scales=A[10], H=200), SHAPE), (dict(k=17), SHAPE),
-    (dict(E=513), SHAPE), (dict(H=12), SHAPE),
+    (dict(E=1025), SHAPE), (dict(H=12), SHAPE),
+    (dict(E=600, xdt=0, pdt=0), DTYPE),
     (dict(cap=O.rows_capacity(100, 16, 2, 4) - 1), CAP), (dict(wsb=10), WS),
     (dict(rows=A[7] + 4), ALIGN), (dict(ws=A[6] + 8), ALIGN),
     (dict(rows=A[0]), ALIAS), (dict(rows=A[6]), ALIAS),
@@ -191,7 +194,7 @@ def _noalloc_cap(T, E, k, pad):
     (dict(pdt=2, scales=A[8], H=200), SHAPE),
     (dict(cap=O.rows_capacity(100, 16, 2, 4) - 1), CAP),
     (dict(rows=A[5] + 4), ALIGN), (dict(rows=A[0]), ALIAS),
-    (dict(tok_row=A[1]), ALIAS), (dict(k=0), SHAPE), (dict(E=513), SHAPE),
+    (dict(tok_row=A[1]), ALIAS), (dict(k=0), SHAPE), (dict(E=1025), SHAPE),
     # more slots and tile counts than the 8 MiB static scratch holds
     (dict(T=300000, H=8, k=8, E=16, cap=_noalloc_cap(300000, 16, 8, 4)),
      SCRATCH),

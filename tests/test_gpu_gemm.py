@@ -35,6 +35,9 @@ CASES = {
     # segments of ~300 rows: several row tiles per expert, a half-empty last
     "e4_long_segments": (C["dsv3_prefill"].with_shape(T=600, H=256, E=4, k=2,
                                                       pad=128), 384, "f32"),
+    # the most experts (tile map over 1024 segments, many empty)
+    "e1024": (C["moonep_skew"].with_shape(T=300, H=256, E=1024, k=4, pad=8,
+                                          zipf_bias=False), 128, "bf16"),
 }
 
 

@@ -93,6 +93,17 @@ SMALL = {
     "narrow_t5000_e512": C["moonep_skew"].with_shape(T=5000, H=256, E=512,
                                                      zipf_bias=False),
     "narrow_t4100_h64": C["dsv3_decode"].with_shape(T=4100, H=64, E=256),
+    # more than 512 experts: partial logits in expert groups of 256, a
+    # 64-lane top-k per token (12 and 16 logits per lane), the plan kernels;
+    # one workgroup per token up to 512 tokens, else one wave per token; a
+    # single hidden range at H = 64
+    "e1024_t100_k16": C["moonep_skew"].with_shape(T=100, H=256, E=1024, k=16,
+                                                  pad=8, zipf_bias=False),
+    "e1024_t1000_bias": C["moonep_skew"].with_shape(T=1000, H=512, E=1024),
+    "e600_t5000": C["moonep_skew"].with_shape(T=5000, H=384, E=600,
+                                              zipf_bias=False),
+    "e1024_t700_h64": C["moonep_skew"].with_shape(T=700, H=64, E=1024,
+                                                  zipf_bias=False),
 }
 FULL = ["mixtral", "dsv3_decode", "dsv3_prefill", "moonep_skew", "tiny"]
 # gate shapes above 8192 tokens (route only: the dispatch and combine of

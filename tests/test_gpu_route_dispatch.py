@@ -35,6 +35,9 @@ CASES = {
                                                pad=8, zipf_bias=False),
     # beyond 512 tokens: the two calls' launches
     "t513": C["dsv3_decode"].with_shape(T=513, H=512),
+    # more than 512 experts: plan kernel, then the scatter
+    "e1024_t300": C["moonep_skew"].with_shape(T=300, H=256, E=1024, k=8,
+                                              pad=8, zipf_bias=False),
 }
 
 
