@@ -269,12 +269,18 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_fp8_kernel(
       if (i + 1 < kMI) fn = read_frag(base + (kMI * wm + i + 1) * 2048);
       const float si = row_scale(scales, i) * swb;
       f32x4 p[4];
+      // raised wave priority while this step's MFMAs and the previous
+      // step's scale-FMAs issue: the two waves of a SIMD, released together
+      // by each barrier, then drift apart so one's LDS reads overlap the
+      // other's MFMAs (measured 5-9 % faster, same bits)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
       if (i > 0) retire(i - 1);
       else if (b > 0) retire(kMI - 1);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) pp[j] = p[j];
       sp = si;
