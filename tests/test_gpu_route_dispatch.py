@@ -35,6 +35,9 @@ CASES = {
                                                pad=8, zipf_bias=False),
     # beyond 512 tokens: the two calls' launches
     "t513": C["dsv3_decode"].with_shape(T=513, H=512),
+    # narrow one-pass gate (weight under 1 MiB, 4096+ tokens), tile
+    # histogram and parallel scan, then the scatter
+    "narrow_t4100": C["moonep_skew"].with_shape(T=4100, H=256),
     # more than 512 experts: plan kernel, then the scatter
     "e1024_t300": C["moonep_skew"].with_shape(T=300, H=256, E=1024, k=8,
                                               pad=8, zipf_bias=False),
