@@ -129,10 +129,14 @@ __device__ __forceinline__ void clear_group_totals(int32_t* __restrict__ g,
 // logits of experts 16*et + c in v[et] (bias already added).  Each logit
 // becomes a 64-bit key (order-preserving logit key, then inverted expert
 // id), built once; padded experts get key 0.  k rounds of a 16-lane max
-// pick the largest logit, lowest index first on ties; the winner is removed
-// by clearing its high word, which leaves it below every real key (the key
-// of any non-NaN logit has a non-zero high word).  Lane j of the group
-// writes the j-th choice and its renormalised weight.
+// pick the largest logit, lowest index first on ties.  For 4 <= k <= 8
+// (and 8+ keys per lane) each lane first sorts its 8 largest keys (no lane
+// can supply more than k choices) and a round's winner lane drops its head;
+// otherwise (and where SORT8 is off: the sorted list does not fit the
+// registers of 1024-thread workgroups beyond 16 keys per lane) the winner is
+// removed by clearing its high word, which leaves it below every
+// real key (the key of any non-NaN logit has a non-zero high word).  Lane j
+// of the group writes the j-th choice and its renormalised weight.
 // Lane c of a 16-lane group holds expert 16 et + c in v[et], or with QUAD
 // expert 64 (et / 4) + 4 c + et % 4 (four consecutive experts per 16-byte
 // load).
@@ -141,7 +145,61 @@ __device__ __forceinline__ int topk_expert(int et, int c) {
   return QUAD ? 64 * (et >> 2) + 4 * c + (et & 3) : et * 16 + c;
 }
 
-template <int ET, bool QUAD = false>
+// Compare-exchange of 64-bit keys: the larger to a, the smaller to b.
+__device__ __forceinline__ void ce_desc(unsigned long long& a,
+                                        unsigned long long& b) {
+  const bool sw = b > a;
+  const unsigned long long hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+// Keys o .. o + 7 in descending order (Batcher's odd-even merge sort, 19
+// compare-exchanges).
+template <int N>
+__device__ __forceinline__ void sort8_desc(unsigned long long (&q)[N], int o) {
+  ce_desc(q[o + 0], q[o + 1]); ce_desc(q[o + 2], q[o + 3]);
+  ce_desc(q[o + 4], q[o + 5]); ce_desc(q[o + 6], q[o + 7]);
+  ce_desc(q[o + 0], q[o + 2]); ce_desc(q[o + 1], q[o + 3]);
+  ce_desc(q[o + 4], q[o + 6]); ce_desc(q[o + 5], q[o + 7]);
+  ce_desc(q[o + 1], q[o + 2]); ce_desc(q[o + 5], q[o + 6]);
+  ce_desc(q[o + 0], q[o + 4]); ce_desc(q[o + 1], q[o + 5]);
+  ce_desc(q[o + 2], q[o + 6]); ce_desc(q[o + 3], q[o + 7]);
+  ce_desc(q[o + 2], q[o + 4]); ce_desc(q[o + 3], q[o + 5]);
+  ce_desc(q[o + 1], q[o + 2]); ce_desc(q[o + 3], q[o + 4]);
+  ce_desc(q[o + 5], q[o + 6]);
+}
+// This lane's 8 largest keys in descending order (zeros past its ET keys):
+// groups of 8 (the last padded with zeros) sorted, then merged pairwise
+// keeping the top 8 (the largest 8 of two descending lists are
+// max(a_i, b_{7-i}), a bitonic sequence that 12 compare-exchanges sort).
+template <int ET>
+__device__ __forceinline__ void lane_top8(const unsigned long long (&key)[ET],
+                                          unsigned long long (&L)[8]) {
+  constexpr int NG = (ET + 7) / 8;
+  unsigned long long q[8 * NG];
+#pragma unroll
+  for (int i = 0; i < 8 * NG; ++i) q[i] = i < ET ? key[i] : 0ull;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) sort8_desc(q, 8 * g);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) L[i] = q[i];
+#pragma unroll
+  for (int g = 1; g < NG; ++g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned long long b = q[8 * g + 7 - i];
+      L[i] = b > L[i] ? b : L[i];
+    }
+    ce_desc(L[0], L[4]); ce_desc(L[1], L[5]);
+    ce_desc(L[2], L[6]); ce_desc(L[3], L[7]);
+    ce_desc(L[0], L[2]); ce_desc(L[1], L[3]);
+    ce_desc(L[4], L[6]); ce_desc(L[5], L[7]);
+    ce_desc(L[0], L[1]); ce_desc(L[2], L[3]);
+    ce_desc(L[4], L[5]); ce_desc(L[6], L[7]);
+  }
+}
+
+template <int ET, bool QUAD = false, bool SORT8 = true>
 __device__ __forceinline__ void topk_select_write(
     const float (&v)[ET], int t, int T, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -161,17 +219,42 @@ __device__ __forceinline__ void topk_select_write(
   for (int j = 0; j < MOE_MAX_TOPK; ++j) {
     sel_e[j] = 0;
     sel_v[j] = 0.0f;
-    if (j < k) {
-      unsigned long long best = key[0];
+  }
+  // with 8 or more keys per lane and 4 <= k <= 8 (where the one-time sort
+  // costs fewer instructions than k full passes over the keys): a lane can
+  // supply at most k of the choices, so its 8 largest keys are sorted once
+  // and each round's winner lane drops its head
+  if (SORT8 && ET >= 8 && k >= 4 && k <= 8) {
+    unsigned long long L[8];
+    lane_top8<ET>(key, L);
 #pragma unroll
-      for (int et = 1; et < ET; ++et) best = key[et] > best ? key[et] : best;
-      best = max16_u64(best);
-      const uint32_t blo = (uint32_t)best;
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        const unsigned long long best = max16_u64(L[0]);
+        const uint32_t blo = (uint32_t)best;
+        const bool win = (uint32_t)L[0] == blo;
 #pragma unroll
-      for (int et = 0; et < ET; ++et)
-        if ((uint32_t)key[et] == blo) key[et] &= 0xffffffffull;
-      sel_e[j] = (int)(0xffffffffu - blo);
-      sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
+        for (int i = 0; i < 7; ++i) L[i] = win ? L[i + 1] : L[i];
+        L[7] = win ? 0ull : L[7];
+        sel_e[j] = (int)(0xffffffffu - blo);
+        sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        unsigned long long best = key[0];
+#pragma unroll
+        for (int et = 1; et < ET; ++et) best = key[et] > best ? key[et] : best;
+        best = max16_u64(best);
+        const uint32_t blo = (uint32_t)best;
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+          if ((uint32_t)key[et] == blo) key[et] &= 0xffffffffull;
+        sel_e[j] = (int)(0xffffffffu - blo);
+        sel_v[j] = f32_from_order_key((uint32_t)(best >> 32));
+      }
     }
   }
   float ex[MOE_MAX_TOPK];
@@ -987,10 +1070,11 @@ __global__ __launch_bounds__(64 * WAVES) void gate_reduce_quad_kernel(
       logits_dbg[(size_t)t * E + e] = v[et];
   }
   if constexpr (HIST)
-    topk_select_write<ET, true>(v, t, T, E, k, topk_idx, topk_w, tile_bits,
-                                tile_sel, tl);
+    topk_select_write<ET, true, (WAVES < 16 || ET <= 16)>(
+        v, t, T, E, k, topk_idx, topk_w, tile_bits, tile_sel, tl);
   else
-    topk_select_write<ET, true>(v, t, T, E, k, topk_idx, topk_w);
+    topk_select_write<ET, true, (WAVES < 16 || ET <= 16)>(
+        v, t, T, E, k, topk_idx, topk_w);
   if constexpr (HIST) {
     __syncthreads();
     for (int e = tid; e < E; e += NT) {
