@@ -1287,11 +1287,11 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(
 // groups before its own, scans the padded counts over the experts (the
 // offsets; workgroup 0 stores counts and offsets) and turns its tiles'
 // counts into first rows.  No workgroup reads another group's tiles.
+template <int PER>   // experts per thread: E <= 256 * PER
 __global__ __launch_bounds__(256) void expert_scan_groups_kernel(
     int32_t* __restrict__ tile_base, int ntiles, int E, int pad,
     const int32_t* __restrict__ gtot, int ngroups,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  constexpr int PER = MOE_MAX_EXPERTS / 256;   // experts per thread
   constexpr int B = 16;                        // loads in flight
   __shared__ int wsum[4];
   const int tid = threadIdx.x, g = blockIdx.x;
@@ -1931,9 +1931,14 @@ static hipError_t finish_plan(int stage, const int32_t* topk_idx, int T,
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(expert_scan_groups_kernel, dim3(num_groups(T)),
-                     dim3(256), 0, s, tile_base, nt, E, pad, gtot,
-                     num_groups(T), counts, offsets);
+#define MOE_SCAN_G(PERV)                                                      \
+  hipLaunchKernelGGL(expert_scan_groups_kernel<PERV>, dim3(num_groups(T)),    \
+                     dim3(256), 0, s, tile_base, nt, E, pad, gtot,            \
+                     num_groups(T), counts, offsets)
+  if (E <= 256) MOE_SCAN_G(1);
+  else if (E <= 512) MOE_SCAN_G(2);
+  else MOE_SCAN_G(4);
+#undef MOE_SCAN_G
   return hipGetLastError();
 }
 
