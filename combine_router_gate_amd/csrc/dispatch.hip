@@ -235,30 +235,9 @@ __device__ void local_plan(const int32_t* __restrict__ topk_idx, int T, int k,
   }
   __syncthreads();
   if (tid < 64) {
-    // exclusive scan of the padded counts: lane l owns experts [8l, 8l+8)
-    constexpr int PER = MOE_MAX_EXPERTS / 64;
-    int loc[PER];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid * PER + i;
-      loc[i] = e < E ? off[e] : 0;
-      sum += loc[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += v;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid * PER + i;
-      if (e < E) off[e] = run;
-      run += loc[i];
-    }
-    if (tid == 63) off[E] = incl;
+    // exclusive scan of the padded counts
+    const int total = wave_exclusive_scan(off, E, nullptr);
+    if (tid == 0) off[E] = total;
   }
   __syncthreads();
   for (int e = tid; e < E; e += nthr) {

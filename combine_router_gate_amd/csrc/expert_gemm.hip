@@ -57,31 +57,14 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
     off[e] = o < 0 ? 0 : o > cap ? cap : o;
   }
   __syncthreads();
+  for (int e = tid; e < E; e += 512) {
+    const int seg = off[e + 1] - off[e];
+    start[e] = seg > 0 ? (seg + tm - 1) / tm : 0;
+  }
+  __syncthreads();
   if (tid < 64) {
-    constexpr int PER = MOE_MAX_EXPERTS / 64;
-    int loc[PER];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid * PER + i;
-      const int seg = e < E ? off[e + 1] - off[e] : 0;
-      loc[i] = seg > 0 ? (seg + tm - 1) / tm : 0;
-      sum += loc[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (tid >= d) incl += o;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid * PER + i;
-      if (e < E) start[e] = run;
-      run += loc[i];
-    }
-    if (tid == 63) start[E] = incl;
+    const int total = wave_exclusive_scan(start, E, nullptr);
+    if (tid == 0) start[E] = total;
   }
   __syncthreads();
   const int total = start[E];

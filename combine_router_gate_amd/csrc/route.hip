@@ -1418,33 +1418,9 @@ __device__ void small_plan(const int32_t* __restrict__ topk_idx, int T, int k,
   }
   __syncthreads();
   if (tid < 64) {
-    // exclusive scan of the padded counts: lane l owns experts [8l, 8l+8)
-    constexpr int PER = MOE_MAX_EXPERTS / 64;
-    int loc[PER];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid * PER + i;
-      loc[i] = e < E ? ecnt[e] : 0;
-      sum += loc[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (tid >= off) incl += o;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid * PER + i;
-      if (e < E) {
-        ecnt[e] = run;
-        offsets[e] = run;
-      }
-      run += loc[i];
-    }
-    if (tid == 63) offsets[E] = incl;
+    // exclusive scan of the padded counts (also the offsets)
+    const int total = wave_exclusive_scan(ecnt, E, offsets);
+    if (tid == 0) offsets[E] = total;
   }
   __syncthreads();
   for (int e = tid; e < E; e += NT) {
