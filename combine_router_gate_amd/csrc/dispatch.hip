@@ -26,6 +26,7 @@
 // destination.  Extra workgroups mark padding rows (row_src = -1) in the
 // same launch.
 #include "moe_device.h"
+#include "moe_scan.h"
 #include "moe_launch.h"
 
 namespace moe {

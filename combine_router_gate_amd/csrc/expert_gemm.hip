@@ -38,6 +38,7 @@
 
 #include "expert_gemm.h"
 #include "moe_device.h"
+#include "moe_scan.h"
 
 namespace moe {
 

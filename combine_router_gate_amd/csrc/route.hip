@@ -46,6 +46,7 @@
 //    then an LDS scan over experts) and leaves, in place, the first row of
 //    every (tile, expert) run.
 #include "moe_device.h"
+#include "moe_scan.h"
 #include "moe_launch.h"
 
 namespace moe {
