@@ -237,7 +237,8 @@ __device__ void local_plan(const int32_t* __restrict__ topk_idx, int T, int k,
   __syncthreads();
   if (tid < 64) {
     // exclusive scan of the padded counts
-    const int total = wave_exclusive_scan(off, E, nullptr);
+    const int total =
+        wave_exclusive_scan<MOE_MAX_EXPERTS / 64>(off, E, nullptr);
     if (tid == 0) off[E] = total;
   }
   __syncthreads();

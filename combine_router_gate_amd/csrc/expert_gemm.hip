@@ -64,7 +64,8 @@ __global__ __launch_bounds__(512) void gemm_tile_map_kernel(
   }
   __syncthreads();
   if (tid < 64) {
-    const int total = wave_exclusive_scan(start, E, nullptr);
+    const int total =
+        wave_exclusive_scan<MOE_MAX_EXPERTS / 64>(start, E, nullptr);
     if (tid == 0) start[E] = total;
   }
   __syncthreads();

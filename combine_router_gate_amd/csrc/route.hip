@@ -1420,7 +1420,8 @@ __device__ void small_plan(const int32_t* __restrict__ topk_idx, int T, int k,
   __syncthreads();
   if (tid < 64) {
     // exclusive scan of the padded counts (also the offsets)
-    const int total = wave_exclusive_scan(ecnt, E, offsets);
+    const int total =
+        wave_exclusive_scan<MOE_MAX_EXPERTS / 64>(ecnt, E, offsets);
     if (tid == 0) offsets[E] = total;
   }
   __syncthreads();
