@@ -19,6 +19,7 @@ HIP-graph replay of the layer.
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -431,7 +432,7 @@ def measure_expert_gemm(cfg, moe, d, p, dev, iters=5):
 
 
 def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
-                           iters=20):
+                           iters=20, reps=7):
     """Small batches: moe_route_dispatch (route + scatter, no plan kernel)
     against moe_route followed by moe_dispatch, alone and as a whole layer
     step with the combine; each timed over iters back-to-back launches."""
@@ -466,13 +467,20 @@ def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / iters
 
-    r = {"fused_us": timed(fused), "separate_us": timed(separate)}
-    r["fused_step_us"] = timed(lambda: (fused(), combine()))
-    r["separate_step_us"] = timed(lambda: (separate(), combine()))
-    r = {kk: round(v, 2) for kk, v in r.items()}
+    legs = {"fused_us": fused, "separate_us": separate,
+            "fused_step_us": lambda: (fused(), combine()),
+            "separate_step_us": lambda: (separate(), combine())}
+    # the legs alternate, reps rounds, and each reports its median: these
+    # launch-bound timings drift with the clock over a run
+    samples = {kk: [] for kk in legs}
+    for _ in range(reps):
+        for kk, fn in legs.items():
+            samples[kk].append(timed(fn))
+    r = {kk: round(statistics.median(v), 2) for kk, v in samples.items()}
     r["how"] = (f"{iters} back-to-back calls: route+dispatch in one call "
                 "(plan rebuilt in every scatter workgroup) vs moe_route then "
-                "moe_dispatch; step = with the combine")
+                "moe_dispatch; step = with the combine; median of "
+                f"{reps} alternating rounds")
     return r
 
 
