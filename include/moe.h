@@ -47,6 +47,12 @@
  *     errors are detected before anything is enqueued and leave every output
  *     untouched; MOE_ERR_HIP reports a failed launch (see moe_last_hip_error).
  *     T == 0 is valid and enqueues nothing except what the entry point says.
+ *   - Non-finite data.  The arithmetic is specified for finite inputs, and
+ *     no call scans its data for NaN or infinities: they propagate (a NaN
+ *     logit ranks above +Inf; an infinite element gives its fp8 block an
+ *     infinite scale).  Whatever the data, every kernel keeps its accesses
+ *     in bounds: expert ids outside [0, E) and rows outside the buffer are
+ *     skipped, not followed.
  *   - Determinism.  No floating-point atomics are used: identical inputs give
  *     bit-identical outputs on every run.
  *   - Thread safety.  The library keeps no mutable state besides the last
