@@ -26,15 +26,19 @@
 //    narrow gate (weight under 1 MiB, 4096 to 32768 tokens) skips the
 //    split: gate_topk_narrow_kernel runs 32 tokens x all experts per
 //    workgroup, each streaming the whole weight from L2 through LDS, with
-//    the top-k in its epilogue.  x is
-//    read with ordinary (allocating) loads, so the dispatch that reads it
-//    next finds much of it still in the memory-attached cache.
+//    the top-k in its epilogue.  Above 512 experts (bf16) the partial
+//    logits come in expert groups of 256 and the top-k of a token takes a
+//    whole wave.  x is read with ordinary (allocating) loads, so the
+//    dispatch that reads it next finds much of it still in the
+//    memory-attached cache.
 //  * E < 64 (memory-bound gate): the 4 waves split the hidden dimension of a
 //    16-token tile and reduce their partial logits through LDS in a fixed
 //    order, so four times as many workgroups stream x.
 //  * Top-k: the 16 lanes of a lane group hold all logits of one token; k
 //    rounds of a 16-lane max over 64-bit keys (order-preserving logit key,
-//    then inverted expert id) give the lowest-index tie-break exactly.
+//    then inverted expert id) give the lowest-index tie-break exactly; for
+//    4 <= k <= 8 each lane first sorts its 8 largest keys, so a round only
+//    compares list heads.
 //    Weights are exp(l_j - l_max) / sum over the chosen, i.e. the full
 //    softmax renormalised over the chosen experts (the all-expert
 //    denominator cancels).
@@ -42,9 +46,11 @@
 //    assembled with ds_or_b64; its popcount is the tile count and the
 //    popcount of the bits below a token is that token's rank, which fixes a
 //    stable, deterministic slot order with no global atomics.
-//  * Scan: one workgroup scans the [tiles, E] counts (chunked over tiles,
-//    then an LDS scan over experts) and leaves, in place, the first row of
-//    every (tile, expert) run.
+//  * Scan: the [tiles, E] counts become, in place, the first row of every
+//    (tile, expert) run.  After a split or narrow gate one workgroup per
+//    group of 16 tiles does it from per-group expert totals that the
+//    histogram producers accumulate; otherwise one workgroup scans all
+//    tiles; up to 512 tokens one workgroup plans everything in LDS.
 #include "moe_device.h"
 #include "moe_scan.h"
 #include "moe_launch.h"
