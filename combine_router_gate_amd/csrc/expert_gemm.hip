@@ -21,18 +21,22 @@
 //  * The weight tile is the instruction's first operand, so each lane ends
 //    up with 4 consecutive output columns of one row: one row scale per
 //    lane and block, 8-byte bf16 stores.
-//  * A workgroup computes a 128x256 tile with 8 waves (two per SIMD, 64x64
-//    each; 256-row tiles need more registers than a wave has and spill);
-//    operands are staged through two LDS stages, loaded through registers
-//    (direct global->LDS copies measured slower on this part).  Global
-//    loads are coalesced (8 lanes per 128-byte row segment; with one row
-//    per lane the address unit handled every 16-byte access separately and
-//    was 72% busy) and stored row by row in LDS with an XOR swizzle of the
-//    16-byte pieces that keeps both those writes and the fragment reads free
-//    of bank conflicts.  The activation scales of the tile's rows, for all
-//    K blocks, are copied to LDS once at its start with coalesced loads.
-//  * Work order: all column tiles of one row tile are consecutive, so the
-//    row tile's activations stay cached while the expert's weights stream.
+//  * A workgroup computes a 256x256 tile with 8 waves (two per SIMD, 128x64
+//    each: 12 fragments read from LDS per 32 MFMAs, accumulators in 128
+//    VGPRs).  Operands reach LDS through direct global->LDS copies into two
+//    stages (no staging registers, which is what lets the 256-row tile fit),
+//    stored row by row with an XOR swizzle of the 16-byte pieces that keeps
+//    the fragment reads free of bank conflicts; the activation scales of a
+//    block travel with it.
+//  * Each wave's block is software-pipelined: the next activation fragment
+//    is read while the current MFMAs run, and their products are scaled
+//    into the accumulators during the next step, under a raised wave
+//    priority so the two waves of a SIMD drift apart and one's LDS reads
+//    overlap the other's MFMAs.
+//  * Work order: workgroups land on the 8 XCDs round-robin; column tiles are
+//    placed so each one stays on one XCD for every row tile, so an expert's
+//    weight panels are read into one L2 while its activation rows are
+//    shared across XCDs.
 //  * Row tiles come from a tile map built on the device from offsets, so no
 //    count ever returns to the host.
 
