@@ -434,8 +434,10 @@ def measure_expert_gemm(cfg, moe, d, p, dev, iters=5):
 def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
                            iters=20, reps=7):
     """Small batches: moe_route_dispatch (route + scatter, no plan kernel)
-    against moe_route followed by moe_dispatch, alone and as a whole layer
-    step with the combine; each timed over iters back-to-back launches."""
+    against moe_route followed by moe_dispatch and (bf16, up to 256 tokens
+    and 512 experts) against moe_route_dispatch_one_launch, alone and as a
+    whole layer step with the combine; each timed over iters back-to-back
+    launches."""
     import torch
     T, E, k, pad = cfg.T, cfg.E, cfg.k, cfg.pad
     sp = stream.cuda_stream
@@ -446,6 +448,12 @@ def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
                                p["workspace"], d["payload_dtype"], d["rows"],
                                d["row_scales"], d["row_src"], d["tok_row"],
                                sp)
+
+    def one_launch():
+        moe.moe_route_dispatch_one_launch(
+            x, w, bias, k, pad, p["topk_idx"], p["topk_w"], p["counts"],
+            p["offsets"], None, p["workspace"], d["payload_dtype"], d["rows"],
+            d["row_scales"], d["row_src"], d["tok_row"], sp)
 
     def separate():
         moe.moe_route(x, w, bias, k, pad, p["topk_idx"], p["topk_w"],
@@ -470,6 +478,10 @@ def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
     legs = {"fused_us": fused, "separate_us": separate,
             "fused_step_us": lambda: (fused(), combine()),
             "separate_step_us": lambda: (separate(), combine())}
+    one = (T <= 256 and E <= 512 and x.dtype == torch.bfloat16)
+    if one:
+        legs["one_launch_us"] = one_launch
+        legs["one_launch_step_us"] = lambda: (one_launch(), combine())
     # the legs alternate, reps rounds, and each reports its median: these
     # launch-bound timings drift with the clock over a run
     samples = {kk: [] for kk in legs}
@@ -479,8 +491,11 @@ def measure_route_dispatch(cfg, moe, x, w, bias, p, d, y, combine, stream,
     r = {kk: round(statistics.median(v), 2) for kk, v in samples.items()}
     r["how"] = (f"{iters} back-to-back calls: route+dispatch in one call "
                 "(plan rebuilt in every scatter workgroup) vs moe_route then "
-                "moe_dispatch; step = with the combine; median of "
-                f"{reps} alternating rounds")
+                "moe_dispatch"
+                + (" vs moe_route_dispatch_one_launch (one kernel, two "
+                   "grid-wide waits)" if one else "")
+                + f"; step = with the combine; median of {reps} alternating "
+                "rounds")
     return r
 
 

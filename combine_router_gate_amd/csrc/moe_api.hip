@@ -246,14 +246,16 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
       (hipStream_t)stream));
 }
 
-int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
-                       const void* w_gate, int E, const float* bias, int k,
-                       int pad, int32_t* topk_idx, float* topk_w,
-                       int32_t* counts, int32_t* offsets, float* logits_dbg,
-                       void* workspace, size_t workspace_bytes,
-                       int payload_dtype, void* rows, size_t rows_capacity,
-                       float* row_scales, int32_t* row_src, int32_t* tok_row,
-                       void* stream) {
+namespace {
+// Arguments of moe_route_dispatch (and of its one-launch form).
+int check_route_dispatch(const void* x, int x_dtype, int T, int H,
+                         const void* w_gate, int E, const float* bias, int k,
+                         int pad, int32_t* topk_idx, float* topk_w,
+                         int32_t* counts, int32_t* offsets, float* logits_dbg,
+                         void* workspace, size_t workspace_bytes,
+                         int payload_dtype, void* rows, size_t rows_capacity,
+                         float* row_scales, int32_t* row_src,
+                         int32_t* tok_row) {
   int st = check_route_shape(T, E, k, pad);
   if (st != MOE_OK) return st;
   if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
@@ -292,6 +294,23 @@ int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
                        {row_src, rows_capacity * 4},
                        {tok_row, (size_t)T * k * 4}};
   if (any_overlap(outs, 10, ins, 3)) return MOE_ERR_ALIAS;
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
+                       const void* w_gate, int E, const float* bias, int k,
+                       int pad, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* offsets, float* logits_dbg,
+                       void* workspace, size_t workspace_bytes,
+                       int payload_dtype, void* rows, size_t rows_capacity,
+                       float* row_scales, int32_t* row_src, int32_t* tok_row,
+                       void* stream) {
+  const int st = check_route_dispatch(
+      x, x_dtype, T, H, w_gate, E, bias, k, pad, topk_idx, topk_w, counts,
+      offsets, logits_dbg, workspace, workspace_bytes, payload_dtype, rows,
+      rows_capacity, row_scales, row_src, tok_row);
+  if (st != MOE_OK) return st;
   if (trace_on())
     std::fprintf(stderr,
                  "moe_route_dispatch T=%d H=%d E=%d k=%d pad=%d dtype=%d "
@@ -301,6 +320,37 @@ int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
       x, w_gate, x_dtype, bias, T, H, E, k, pad, topk_idx, topk_w, counts,
       offsets, logits_dbg, workspace, payload_dtype, rows, rows_capacity,
       row_scales, row_src, tok_row, (hipStream_t)stream));
+}
+
+int moe_route_dispatch_one_launch(
+    const void* x, int x_dtype, int T, int H, const void* w_gate, int E,
+    const float* bias, int k, int pad, int32_t* topk_idx, float* topk_w,
+    int32_t* counts, int32_t* offsets, float* logits_dbg, void* workspace,
+    size_t workspace_bytes, int payload_dtype, void* rows,
+    size_t rows_capacity, float* row_scales, int32_t* row_src,
+    int32_t* tok_row, void* stream) {
+  const int st = check_route_dispatch(
+      x, x_dtype, T, H, w_gate, E, bias, k, pad, topk_idx, topk_w, counts,
+      offsets, logits_dbg, workspace, workspace_bytes, payload_dtype, rows,
+      rows_capacity, row_scales, row_src, tok_row);
+  if (st != MOE_OK) return st;
+  if (x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T > moe::kOneLaunchMaxT || E > moe::kGateWideE) return MOE_ERR_SHAPE;
+  if (T == 0)
+    return moe_route_dispatch(x, x_dtype, T, H, w_gate, E, bias, k, pad,
+                              topk_idx, topk_w, counts, offsets, logits_dbg,
+                              workspace, workspace_bytes, payload_dtype, rows,
+                              rows_capacity, row_scales, row_src, tok_row,
+                              stream);
+  if (trace_on())
+    std::fprintf(stderr,
+                 "moe_route_dispatch_one_launch T=%d H=%d E=%d k=%d pad=%d "
+                 "payload=%d cap=%zu\n",
+                 T, H, E, k, pad, payload_dtype, rows_capacity);
+  return hip_status(moe::launch_route_dispatch_one_launch(
+      x, w_gate, bias, T, H, E, k, pad, topk_idx, topk_w, counts, offsets,
+      logits_dbg, workspace, payload_dtype, rows, rows_capacity, row_scales,
+      row_src, tok_row, (hipStream_t)stream));
 }
 
 size_t moe_noalloc_scratch_bytes(int T, int E, int k) {

@@ -125,6 +125,16 @@ hipError_t launch_route_dispatch(const void* x, const void* w, int xdt,
                                  int32_t* row_src, int32_t* tok_row,
                                  hipStream_t s);
 
+// moe_route_dispatch in one launch for T <= kOneLaunchMaxT bf16 tokens and
+// E <= kGateWideE (grid-wide waits between gate, top-k and scatter)
+constexpr int kOneLaunchMaxT = 256;
+hipError_t launch_route_dispatch_one_launch(
+    const void* x, const void* w, const float* bias, int T, int H, int E,
+    int k, int pad, int32_t* topk_idx, float* topk_w, int32_t* counts,
+    int32_t* offsets, float* logits_dbg, void* workspace, int pdt, void* rows,
+    size_t capacity, float* row_scales, int32_t* row_src, int32_t* tok_row,
+    hipStream_t s);
+
 // moe_dispatch with its tile plan rebuilt in the library's static scratch
 hipError_t launch_dispatch_noalloc(const void* x, int xdt, int T, int H,
                                    const int32_t* topk_idx, int k, int E,

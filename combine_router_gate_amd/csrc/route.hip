@@ -51,9 +51,10 @@
 //    group of 16 tiles does it from per-group expert totals that the
 //    histogram producers accumulate; otherwise one workgroup scans all
 //    tiles; up to 512 tokens one workgroup plans everything in LDS.
-#include "moe_device.h"
-#include "moe_scan.h"
-#include "moe_launch.h"
+#include "scatter_device.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace moe {
 
@@ -714,13 +715,13 @@ __global__ __launch_bounds__(512, 1) void gate_topk_narrow_kernel(
 // gate_reduce_quad_kernel / gate_reduce_small_kernel add the ranges in
 // ascending order.  Expert groups let few tokens spread over many
 // workgroups with fewer hidden ranges (fewer partial logits to add).
+// Workgroup (bx, by, bz) of that grid (256 threads).
 template <int EPW, int TT, int PQ, int D, int DX = D>
-__global__ __launch_bounds__(256, 1) void gate_partial_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
-    int H, int E, int KR, int eps, float* __restrict__ partial,
-    int32_t* __restrict__ gzero, int gzero_n) {
-  clear_group_totals(gzero, gzero_n);
-  const int e0 = blockIdx.z * 64 * EPW;    // first expert of the group
+__device__ __forceinline__ void gate_partial_block(
+    int bx, int by, int bz, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ w, int T, int H, int E, int KR, int eps,
+    float* __restrict__ partial) {
+  const int e0 = bz * 64 * EPW;            // first expert of the group
   constexpr int TTOK = 16 * TT;            // tokens of the workgroup
   constexpr int KS = 32 * PQ;              // k per super-step
   constexpr int RB = 2 * KS;               // bytes of one x row per step
@@ -734,8 +735,8 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int t0 = blockIdx.x * TTOK;
-  const int ks = blockIdx.y;
+  const int t0 = bx * TTOK;
+  const int ks = by;
   const int k_lo = ks * KR;
   const int k_hi = min(H, k_lo + KR);
   const int nss = (k_hi - k_lo + KS - 1) / KS;
@@ -848,6 +849,16 @@ __global__ __launch_bounds__(256, 1) void gate_partial_kernel(
         if (t < T) out[(size_t)t * eps + e] = acc[tt][et][i];
       }
     }
+}
+
+template <int EPW, int TT, int PQ, int D, int DX = D>
+__global__ __launch_bounds__(256, 1) void gate_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
+    int H, int E, int KR, int eps, float* __restrict__ partial,
+    int32_t* __restrict__ gzero, int gzero_n) {
+  clear_group_totals(gzero, gzero_n);
+  gate_partial_block<EPW, TT, PQ, D, DX>(blockIdx.x, blockIdx.y, blockIdx.z, x,
+                                         w, T, H, E, KR, eps, partial);
 }
 
 // The same partial logits for many tokens (the same MFMAs in the same order
@@ -1474,8 +1485,8 @@ __device__ __forceinline__ unsigned long long max64_u64(unsigned long long v) {
   return m;
 }
 
-// Reduction of the split gate for few tokens: a workgroup of 8 waves covers
-// TPW tokens with WPT = 8 / TPW waves each.  Wave p of a token adds the
+// Reduction of the split gate for few tokens: a workgroup of RW waves (8 in
+// gate_reduce_small_kernel) covers TPW tokens with WPT = RW / TPW waves each.  Wave p of a token adds the
 // ranges p, p + WPT, ... in ascending order, each lane holding C4 groups of
 // 4 consecutive experts (16-byte loads across the whole logit row); the
 // token's first wave adds its WPT wave sums in wave order (fixed order: the
@@ -1483,18 +1494,19 @@ __device__ __forceinline__ unsigned long long max64_u64(unsigned long long v) {
 // (same 64-bit keys and tie-break as topk_select_write).  The plan follows
 // as plan_small_kernel: a separate launch costs less than having the last
 // workgroup plan after device-scope release/acquire fences in every one.
-template <int C4, int TPW>
-__global__ __launch_bounds__(512) void gate_reduce_small_kernel(
-    const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
-    const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+// Workgroup blk of RW waves (TPW tokens of RW / TPW waves each).
+template <int C4, int TPW, int RW>
+__device__ __forceinline__ void gate_reduce_small_block(
+    int blk, const float* __restrict__ partial, int S, int EPS, int T, int E,
+    int k, const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits_dbg) {
-  constexpr int RW = 8, B = 8;                  // waves, ranges in flight
+  constexpr int B = 8;                          // ranges in flight
   constexpr int WPT = RW / TPW;                 // waves per token
   __shared__ f32x4 red[RW * 64 * C4];           // wave sums
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int tk = wv / WPT, part = wv - tk * WPT;
-  const int t = blockIdx.x * TPW + tk;
+  const int t = blk * TPW + tk;
   const bool live = t < T;
   const int tc = live ? t : T - 1;
   const int nc4 = EPS / 4;                      // 16-byte groups of a row
@@ -1581,6 +1593,101 @@ __global__ __launch_bounds__(512) void gate_reduce_small_kernel(
       topk_w[(size_t)t * k + lane] = ex / den;
     }
   }
+}
+
+template <int C4, int TPW>
+__global__ __launch_bounds__(512) void gate_reduce_small_kernel(
+    const float* __restrict__ partial, int S, int EPS, int T, int E, int k,
+    const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ logits_dbg) {
+  gate_reduce_small_block<C4, TPW, 8>(blockIdx.x, partial, S, EPS, T, E, k,
+                                      bias, topk_idx, topk_w, logits_dbg);
+}
+
+
+// ------------------------------------------------------------------ one launch
+
+// Arrival counters of the one-launch path's grid-wide waits, per GPU: [0]
+// all arrivals, [32 (1 + x)] the arrivals of the workgroups on XCD x.  They
+// only grow; the host passes the value of [0] at the start of each call.
+__device__ __align__(256) unsigned long long g_one_launch_bar[9 * 32];
+
+// Every workgroup of a grid of G (a multiple of 8; workgroup i runs on XCD
+// i % 8) waits here until all G have arrived for the n-th time in this call.
+// What a workgroup wrote before the wait is visible to every workgroup after
+// it: each arrival follows a device-scope release, the last arrival of an
+// XCD acquires its XCD's arrivals and adds them to the global count with a
+// release, and every workgroup acquires once it sees the count complete.
+// The spin is bounded (2^20 polls, on the order of a second): calls that
+// overlap on one GPU, which the entry point rules out, could then give wrong
+// results but cannot hang the GPU.
+__device__ void one_launch_wait(int n, int G, unsigned long long gbase) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long nx = (unsigned long long)(G / 8);
+    unsigned long long* xc = &g_one_launch_bar[32 * (1 + (blockIdx.x & 7))];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned long long t = __hip_atomic_fetch_add(
+        xc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t + 1 == gbase / 8 + (unsigned long long)n * nx) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_fetch_add(&g_one_launch_bar[0], nx, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const unsigned long long target = gbase + (unsigned long long)n * G;
+    for (long i = 0; i < (1l << 20); ++i) {
+      if (__hip_atomic_load(&g_one_launch_bar[0], __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT) >= target)
+        break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// Gate, top-k, plan and scatter of T <= 256 bf16 tokens in one launch: the
+// split gate's partial logits (workgroups as gate_partial_kernel's grid of
+// tiles x ranges x expert groups), a grid-wide wait, the reduction and top-k
+// of one token per workgroup (4 waves share its ranges), a second wait, then
+// every workgroup rebuilds the plan in LDS and runs its share of the scatter
+// blocks and the padding fill, as plan_dispatch_small_kernel does.
+template <int C4, int KMAX, int MODE>
+__global__ __launch_bounds__(256) void route_dispatch_one_launch_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int T, int H, int E, int k, int pad,
+    int KR, int S, int tiles, int eg, float* __restrict__ part,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits_dbg, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, unsigned char* __restrict__ rows,
+    long long capacity, float* __restrict__ row_scales,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ tok_row,
+    int tok_blocks, int hsplit, unsigned long long gbase) {
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int eps = 64 * eg;
+  const int ngate = tiles * S * eg;
+  for (int b = wg; b < ngate; b += G) {
+    gate_partial_block<1, 2, 2, 2>(b % tiles, (b / tiles) % S,
+                                   b / (tiles * S), x, w, T, H, E, KR, eps,
+                                   part);
+    __syncthreads();
+  }
+  one_launch_wait(1, G, gbase);
+  for (int t = wg; t < T; t += G) {
+    gate_reduce_small_block<C4, 1, 4>(t, part, S, eps, T, E, k, bias,
+                                      topk_idx, topk_w, logits_dbg);
+    __syncthreads();
+  }
+  one_launch_wait(2, G, gbase);
+  extern __shared__ unsigned long long plan_lds[];
+  LocalPlan p = local_plan_arrays(plan_lds, T, E);
+  local_plan(topk_idx, T, k, E, pad, p.bits, p.base, p.cnt, p.off);
+  const int nblk = tok_blocks + kDispatchFillBlocks;
+  for (int b = wg; b < nblk; b += G)
+    plan_dispatch_block<KMAX, MODE, 1>(
+        b, reinterpret_cast<const unsigned char*>(x), 2, T, H, topk_idx, k, E,
+        counts, offsets, rows, capacity, row_scales, row_src, tok_row,
+        tok_blocks, hsplit, p);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1996,6 +2103,84 @@ hipError_t launch_route_dispatch(const void* x, const void* w, int xdt,
   return launch_dispatch(x, xdt, T, H, topk_idx, k, E, counts, offsets,
                          workspace, pdt, rows, capacity, row_scales, row_src,
                          tok_row, s);
+}
+
+// The one-launch path's grid: at most one workgroup per compute unit (so all
+// are resident together), a multiple of 8.  Its arrival count per GPU is
+// kept on the host: the device counters start at 0 and grow by 2 G a call.
+namespace {
+constexpr int kOneLaunchMaxDevices = 64;
+std::atomic<unsigned long long> g_one_launch_arrivals[kOneLaunchMaxDevices];
+std::atomic<int> g_one_launch_cus[kOneLaunchMaxDevices];
+}  // namespace
+
+hipError_t launch_route_dispatch_one_launch(
+    const void* x, const void* w, const float* bias, int T, int H, int E,
+    int k, int pad, int32_t* topk_idx, float* topk_w, int32_t* counts,
+    int32_t* offsets, float* logits_dbg, void* workspace, int pdt, void* rows,
+    size_t capacity, float* row_scales, int32_t* row_src, int32_t* tok_row,
+    hipStream_t s) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kOneLaunchMaxDevices) return hipErrorInvalidDevice;
+  int cus = g_one_launch_cus[dev].load();
+  if (cus == 0) {
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                                dev);
+    if (err != hipSuccess) return err;
+    g_one_launch_cus[dev].store(cus);
+  }
+  // the split gate's geometry for few tokens (as launch_gate_typed)
+  const int epw = gate_epw(E);
+  const int tiles = (T + 31) / 32;
+  const int eg = epw;
+  int S = (224 + tiles * eg - 1) / (tiles * eg);
+  S = std::min(S, std::min(split_max(T), (H + 63) / 64));
+  const int KR = ((H + S - 1) / S + 63) / 64 * 64;
+  S = (H + KR - 1) / KR;
+  const int ngate = tiles * S * eg;
+  const int G = std::min((ngate + 7) / 8 * 8, cus / 8 * 8);
+  if (G < 8) return hipErrorInvalidConfiguration;
+  float* part = (float*)((unsigned char*)workspace + ws_tile_bytes(T, E) +
+                         ws_rank_bytes(T, k));
+  const ScatterShape g = scatter_shape(DT_BF16, pdt, T, H, false);
+  const size_t lds = local_plan_lds_bytes(T, E);
+  const unsigned long long gbase =
+      g_one_launch_arrivals[dev].fetch_add(2ull * (unsigned long long)G);
+  const uint16_t* xb = (const uint16_t*)x;
+  const uint16_t* wb = (const uint16_t*)w;
+  unsigned char* rb = (unsigned char*)rows;
+  const long long cap = (long long)capacity;
+#define MOE_OL(C4V, KV, MV)                                                    \
+  hipLaunchKernelGGL((route_dispatch_one_launch_kernel<C4V, KV, MV>), dim3(G), \
+                     dim3(256), lds, s, xb, wb, bias, T, H, E, k, pad, KR, S,  \
+                     tiles, eg, part, topk_idx, topk_w, logits_dbg, counts,    \
+                     offsets, rb, cap, row_scales, row_src, tok_row,           \
+                     g.tblocks, g.hs, gbase)
+#define MOE_OL_M(C4V, KV)                                                      \
+  do {                                                                         \
+    if (g.mode == 0) MOE_OL(C4V, KV, 0);                                       \
+    else MOE_OL(C4V, KV, 1);                                                   \
+  } while (0)
+#define MOE_OL_K(C4V)                                                          \
+  do {                                                                         \
+    if (k <= 1) MOE_OL_M(C4V, 1);                                              \
+    else if (k <= 2) MOE_OL_M(C4V, 2);                                         \
+    else if (k <= 4) MOE_OL_M(C4V, 4);                                         \
+    else if (k <= 8) MOE_OL_M(C4V, 8);                                         \
+    else MOE_OL_M(C4V, 16);                                                    \
+  } while (0)
+  if (epw <= 4) MOE_OL_K(1);
+  else MOE_OL_K(2);
+#undef MOE_OL_K
+#undef MOE_OL_M
+#undef MOE_OL
+  err = hipGetLastError();
+  // a grid that never ran adds nothing to the device counters
+  if (err != hipSuccess)
+    g_one_launch_arrivals[dev].fetch_sub(2ull * (unsigned long long)G);
+  return err;
 }
 
 hipError_t launch_plan(const int32_t* topk_idx, int T, int k, int E, int pad,

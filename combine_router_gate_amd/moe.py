@@ -6,7 +6,8 @@ current HIP stream.  There is no fallback: if the library is not built this
 module raises on first use.
 
 Low-level functions carry the C names (``moe_route``, ``moe_plan``,
-``moe_dispatch``, ``moe_route_dispatch``, ``moe_dispatch_noalloc``,
+``moe_dispatch``, ``moe_route_dispatch``, ``moe_route_dispatch_one_launch``,
+``moe_dispatch_noalloc``,
 ``moe_combine_residual``, ``moe_farskip_aux``,
 ``moe_combine_backward``, ``moe_dispatch_backward``, ``moe_expert_gemm_fp8``,
 ``moe_expert_fixture``) and take preallocated tensors; ``route`` /
@@ -48,6 +49,10 @@ _SIGS = {
     "moe_route_dispatch": (_i, [_vp, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp, _sz,
                                 _vp, _vp, _vp, _vp]),
+    "moe_route_dispatch_one_launch": (_i, [_vp, _i, _i, _i, _vp, _i, _vp, _i,
+                                           _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _sz, _i, _vp, _sz, _vp, _vp, _vp,
+                                           _vp]),
     "moe_noalloc_scratch_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch_noalloc": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp,
                                   _i, _vp, _sz, _vp, _vp, _vp, _vp]),
@@ -193,6 +198,22 @@ def moe_route_dispatch(x, w_gate, bias, k, pad, topk_idx, topk_w, counts,
     _check(st, "moe_route_dispatch")
 
 
+def moe_route_dispatch_one_launch(x, w_gate, bias, k, pad, topk_idx, topk_w,
+                                  counts, offsets, logits_dbg, workspace,
+                                  payload_dtype, rows, row_scales, row_src,
+                                  tok_row, stream=None):
+    T, H = x.shape
+    E = w_gate.shape[0]
+    st = lib().moe_route_dispatch_one_launch(
+        _ptr(x), _dt(x), T, H, _ptr(w_gate), E, _ptr(bias), k, pad,
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+        _ptr(logits_dbg), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, payload_dtype,
+        _ptr(rows), rows.shape[0], _ptr(row_scales), _ptr(row_src),
+        _ptr(tok_row), stream if stream is not None else _stream(x.device))
+    _check(st, "moe_route_dispatch_one_launch")
+
+
 def moe_noalloc_scratch_bytes(T: int, E: int, k: int) -> int:
     return lib().moe_noalloc_scratch_bytes(T, E, k)
 
@@ -306,9 +327,10 @@ def route(x: torch.Tensor, w_gate: torch.Tensor, k: int, pad: int,
 
 def route_dispatch(x: torch.Tensor, w_gate: torch.Tensor, k: int, pad: int,
                    bias: Optional[torch.Tensor] = None, payload: str = "same",
-                   want_logits: bool = False):
+                   want_logits: bool = False, one_launch: bool = False):
     """moe_route + moe_dispatch in one call (small batches skip the plan
-    kernel).  Returns (plan, dispatched) like route() and dispatch()."""
+    kernel; one_launch=True calls moe_route_dispatch_one_launch).  Returns
+    (plan, dispatched) like route() and dispatch()."""
     T, H = x.shape
     E = w_gate.shape[0]
     dev = x.device
@@ -335,10 +357,10 @@ def route_dispatch(x: torch.Tensor, w_gate: torch.Tensor, k: int, pad: int,
         tok_row=torch.empty((T, k), dtype=torch.int32, device=dev),
         payload_dtype=pdt,
     )
-    moe_route_dispatch(x, w_gate, bias, k, pad, p["topk_idx"], p["topk_w"],
-                       p["counts"], p["offsets"], p["logits"], p["workspace"],
-                       pdt, d["rows"], d["row_scales"], d["row_src"],
-                       d["tok_row"])
+    fn = moe_route_dispatch_one_launch if one_launch else moe_route_dispatch
+    fn(x, w_gate, bias, k, pad, p["topk_idx"], p["topk_w"], p["counts"],
+       p["offsets"], p["logits"], p["workspace"], pdt, d["rows"],
+       d["row_scales"], d["row_src"], d["tok_row"])
     return p, d
 
 

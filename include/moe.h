@@ -13,6 +13,8 @@
  *                        with one fp32 scale per 1x128 block)
  *   moe_route_dispatch   moe_route + moe_dispatch in one call (small decode
  *                        batches skip the plan kernel)
+ *   moe_route_dispatch_one_launch
+ *                        the same as one kernel launch (decode batches)
  *   moe_dispatch_noalloc moe_dispatch with no workspace argument (its scratch is
  *                        a static device array), for callers that cannot
  *                        allocate
@@ -31,8 +33,9 @@
  *   - Device pointers.  Every array argument is device memory (HBM) that the
  *     caller allocated and owns; the library never allocates, frees or keeps
  *     a pointer after the call returns.  Its only device memory of its own
- *     is the static scratch array of moe_dispatch_noalloc.  Arrays are dense row-major with the
- *     shapes given below.  Arrays read or written as 16-byte vectors (x,
+ *     is the static scratch array of moe_dispatch_noalloc and the wait
+ *     counters of moe_route_dispatch_one_launch.  Arrays are dense
+ *     row-major with the shapes given below.  Arrays read or written as 16-byte vectors (x,
  *     w_gate, rows, y, shared, residuals, out, gradients of those, workspace)
  *     need 16-byte aligned base addresses; the others their element size.
  *   - Asynchrony.  Each call validates its arguments on the host, then only
@@ -56,8 +59,10 @@
  *   - Determinism.  No floating-point atomics are used: identical inputs give
  *     bit-identical outputs on every run.
  *   - Thread safety.  The library keeps no mutable state besides the last
- *     HIP error code (thread-local) and, for moe_dispatch_noalloc, its
- *     static scratch array and that array's device address per GPU.
+ *     HIP error code (thread-local), for moe_dispatch_noalloc its static
+ *     scratch array and that array's device address per GPU, and for
+ *     moe_route_dispatch_one_launch its wait counters per GPU (device) and
+ *     their running total (host, atomic).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -240,6 +245,37 @@ int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
                        void* rows, size_t rows_capacity, float* row_scales,
                        int32_t* row_src, int32_t* tok_row,
                        void* stream);
+
+/*
+ * moe_route_dispatch_one_launch -- moe_route_dispatch as one kernel launch,
+ * the form of DeepEP's low-latency path for small decode batches (DeepEP
+ * release news, technical overview): gate partial sums, top-k and the
+ * scatter run in one grid whose workgroups wait for each other twice (after
+ * the partial sums, after the top-k) at device-scope counters.  Same
+ * arguments, outputs and errors as moe_route_dispatch, and additionally
+ * x_dtype must be MOE_BF16 (else MOE_ERR_DTYPE), T <= 256 and E <= 512
+ * (else MOE_ERR_SHAPE).  The results equal moe_route_dispatch's up to the
+ * rounding order of the partial-sum reduction (4 waves per token instead of
+ * 8): the logits may differ in the last bits, so choices at exact near-ties
+ * may differ; rows, ranks and weights follow the top-k it made.
+ * Requirements: the grid holds at most one workgroup per compute unit, so
+ * all are resident; calls of this entry point must not overlap on one GPU
+ * (the wait counters are per GPU and only grow; overlapping calls could
+ * give wrong results, never a hang: each wait is bounded).  On MI355X it
+ * measured slower than moe_route_dispatch, which stays the decode path.
+ */
+int moe_route_dispatch_one_launch(const void* x, int x_dtype, int T, int H,
+                                  const void* w_gate, int E,
+                                  const float* bias, int k, int pad,
+                                  int32_t* topk_idx, float* topk_w,
+                                  int32_t* counts, int32_t* offsets,
+                                  float* logits_dbg,
+                                  void* workspace, size_t workspace_bytes,
+                                  int payload_dtype,
+                                  void* rows, size_t rows_capacity,
+                                  float* row_scales,
+                                  int32_t* row_src, int32_t* tok_row,
+                                  void* stream);
 
 /*
  * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate

@@ -45,6 +45,15 @@ hipError_t launch_route_dispatch(const void*, const void*, int, const float*,
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_route_dispatch_one_launch(const void*, const void*,
+                                            const float*, int, int, int, int,
+                                            int, int32_t*, float*, int32_t*,
+                                            int32_t*, float*, void*, int,
+                                            void*, size_t, float*, int32_t*,
+                                            int32_t*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_plan_dispatch_small(const void*, int, int, int,
                                       const int32_t*, int, int, int,
                                       int32_t*, int32_t*, int, void*, size_t,

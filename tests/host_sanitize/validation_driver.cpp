@@ -143,6 +143,21 @@ int main() {
   CASE("route_dispatch INT_MAX", MOE_ERR_SHAPE,
        rd(INT_MAX, 256, MOE_BF16, nullptr, cap, P(6), P(7)));
 
+  auto rd1 = [&](int T, int xdt, size_t cap_) {
+    return moe_route_dispatch_one_launch(
+        P(0), xdt, T, 256, P(1), 16, nullptr, 2, 4, Q<int32_t>(2),
+        Q<float>(3), Q<int32_t>(4), Q<int32_t>(5), nullptr, P(6),
+        moe_workspace_bytes(T > 0 ? T : 1, 16, 2), xdt, P(7), cap_, nullptr,
+        Q<int32_t>(8), Q<int32_t>(9), nullptr);
+  };
+  CASE("route_dispatch_one_launch ok", MOE_OK, rd1(100, MOE_BF16, cap));
+  CASE("route_dispatch_one_launch fp32", MOE_ERR_DTYPE,
+       rd1(100, MOE_F32, cap));
+  CASE("route_dispatch_one_launch T", MOE_ERR_SHAPE,
+       rd1(257, MOE_BF16, moe_rows_capacity(257, 16, 2, 4)));
+  CASE("route_dispatch_one_launch INT_MAX", MOE_ERR_SHAPE,
+       rd1(INT_MAX, MOE_BF16, cap));
+
   // ---------------------------------------------------------- combine
   auto comb = [&](int T, int H, size_t y_rows, void* res_in, void* res_out,
                   void* rnr, void* out) {

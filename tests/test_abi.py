@@ -142,14 +142,14 @@ def test_dispatch_validation(L, no_gpu, kw, want):
     assert _dispatch(L, **kw) == want
 
 
-def _route_dispatch(L, **kw):
+def _route_dispatch(L, fn="moe_route_dispatch", **kw):
     a = dict(x=A[0], xdt=1, T=100, H=256, w=A[1], E=16, bias=None, k=2, pad=4,
              idx=A[2], tw=A[3], counts=A[4], offsets=A[5], dbg=None, ws=A[6],
              wsb=1 << 26, pdt=1, rows=A[7],
              cap=O.rows_capacity(100, 16, 2, 4), scales=None, row_src=A[8],
              tok_row=A[9], stream=None)
     a.update(kw)
-    return L.moe_route_dispatch(
+    return getattr(L, fn)(
         a["x"], a["xdt"], a["T"], a["H"], a["w"], a["E"], a["bias"], a["k"],
         a["pad"], a["idx"], a["tw"], a["counts"], a["offsets"], a["dbg"],
         a["ws"], a["wsb"], a["pdt"], a["rows"], a["cap"], a["scales"],
@@ -170,6 +170,23 @@ def _route_dispatch(L, **kw):
 ])
 def test_route_dispatch_validation(L, no_gpu, kw, want):
     assert _route_dispatch(L, **kw) == want
+
+
+ONE = "moe_route_dispatch_one_launch"
+
+
+@pytest.mark.parametrize("kw,want", [
+    # the checks of moe_route_dispatch come first
+    (dict(x=None), NULL), (dict(rows=None), NULL), (dict(k=17), SHAPE),
+    (dict(cap=O.rows_capacity(100, 16, 2, 4) - 1), CAP), (dict(wsb=10), WS),
+    (dict(rows=A[0]), ALIAS),
+    # then bf16 x, at most 256 tokens and 512 experts
+    (dict(xdt=0, pdt=0), DTYPE),
+    (dict(T=257, cap=O.rows_capacity(257, 16, 2, 4)), SHAPE),
+    (dict(E=600, cap=O.rows_capacity(100, 600, 2, 4)), SHAPE),
+])
+def test_route_dispatch_one_launch_validation(L, no_gpu, kw, want):
+    assert _route_dispatch(L, fn=ONE, **kw) == want
 
 
 def _dispatch_noalloc(L, **kw):
