@@ -229,8 +229,9 @@ int moe_dispatch(const void* x, int x_dtype, int T, int H,
  * the same stream.  Up to 512 tokens the plan kernel between top-k and
  * scatter is skipped: every scatter workgroup rebuilds the plan (tile
  * ballots, counts, padded scan) in its own LDS from topk_idx, so route +
- * scatter take one launch fewer (a grid-wide barrier inside one kernel
- * measured slower on this GPU than the kernel boundary it would replace).
+ * scatter take one launch fewer (moe_route_dispatch_one_launch, below,
+ * replaces the remaining boundaries by grid-wide waits and measured slower
+ * on MI355X).
  * The workspace is then scratch of this call only: it does not hold a plan
  * a later moe_dispatch could read.  Errors as for the two calls.
  */
