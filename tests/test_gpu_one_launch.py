@@ -4,7 +4,9 @@ oracle: logits within tolerance, the top-k exact on the kernel's own logits,
 a valid stable plan, sampled payload rows; the exact plan on integer inputs;
 and the same rows as moe_route_dispatch whenever both chose the same
 experts.  Consecutive calls of different shapes check that the wait
-counters carry over from call to call."""
+counters carry over from call to call; 12 seeded random configurations
+(1-256 tokens, 1-512 experts, k up to 16, bf16 or fp8 payloads, router bias)
+cover the envelope."""
 import numpy as np
 import pytest
 import torch
@@ -130,3 +132,42 @@ def test_one_launch_no_tokens():
     assert (to_host(p["counts"]) == 0).all()
     assert (to_host(p["offsets"]) == 0).all()
     assert (to_host(d["row_src"]) == -1).all()
+
+
+def _draw(rng):
+    E = int(rng.integers(1, 513))
+    k = int(rng.integers(1, min(16, E) + 1))
+    T = int(rng.integers(1, 257))
+    payload = "fp8" if rng.random() < 0.4 else "bf16"
+    H = 128 * int(rng.integers(1, 17)) if payload == "fp8" \
+        else 8 * int(rng.integers(1, 257))
+    pad = int(rng.choice([1, 2, 8, 37, 128]))
+    return I.Config(f"rand_t{T}_h{H}_e{E}_k{k}", T=T, H=H, E=E, k=k, pad=pad,
+                    x_dtype="bf16", payload=payload, y_dtype="bf16",
+                    expert="identity", residual=False,
+                    zipf_bias=bool(rng.random() < 0.4))
+
+
+_rng = np.random.default_rng(20261205)
+RANDOM = [_draw(_rng) for _ in range(12)]
+
+
+@pytest.mark.parametrize("cfg", RANDOM, ids=[c.name for c in RANDOM])
+def test_one_launch_random_shapes(cfg):
+    note(f"one_launch random {cfg.name} pad={cfg.pad} payload={cfg.payload}")
+    wl = I.make_workload(cfg, 11)
+    x, w = to_dev(wl.x), to_dev(wl.w_gate)
+    b = to_dev(wl.bias) if wl.bias is not None else None
+    p, d = moe.route_dispatch(x, w, cfg.k, cfg.pad, bias=b,
+                              payload=_payload(cfg), want_logits=True,
+                              one_launch=True)
+    torch.cuda.synchronize()
+    o = O.route(wl.x.values, wl.w_gate.values, wl.bias, cfg.k, cfg.pad)
+    gl = to_host(p["logits"])
+    assert np.abs(gl.astype(np.float64) - o["logits"]).max() <= LOGIT_TOL
+    gi = to_host(p["topk_idx"])
+    check_topk_own_logits(gi, to_host(p["topk_w"]), gl, cfg.k)
+    check_plan_valid(gi, to_host(p["counts"]), to_host(p["offsets"]),
+                     to_host(d["tok_row"]), to_host(d["row_src"]), cfg.E,
+                     cfg.pad)
+    _sampled_rows(wl, d, cfg)
