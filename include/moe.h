@@ -259,8 +259,10 @@ int moe_route_dispatch(const void* x, int x_dtype, int T, int H,
  * rounding order of the partial-sum reduction (4 waves per token instead of
  * 8): the logits may differ in the last bits, so choices at exact near-ties
  * may differ; rows, ranks and weights follow the top-k it made.
- * Requirements: the grid holds at most one workgroup per compute unit, so
- * all are resident; calls of this entry point must not overlap on one GPU
+ * Requirements: `stream` belongs to the calling thread's current device
+ * (the device whose counters the call uses); the grid holds at most one
+ * workgroup per compute unit, so all are resident; calls of this entry
+ * point must not overlap on one GPU
  * (the wait counters are per GPU and only grow; overlapping calls could
  * give wrong results, never a hang: each wait is bounded).  On MI355X it
  * measured slower than moe_route_dispatch, which stays the decode path.
